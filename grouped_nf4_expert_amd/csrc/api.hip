@@ -1,0 +1,254 @@
+// C ABI of libgnf4: argument validation, path choice and kernel dispatch.
+// Every entry point is declared and documented in include/gnf4.h.
+
+#include <limits.h>
+#include <string.h>
+
+#include "gnf4_internal.h"
+
+namespace gnf4 {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+
+gnf4_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return GNF4_ERR_HIP;
+}
+
+// Rows per group at or below which a group takes the decode path.  One
+// constant for every shape (no per-shape tables): below it a tile of 32
+// MFMA rows would be mostly padding, above it the fp32 decode path's
+// per-row multiply-adds cost more than the matrix core.
+constexpr int kDecodeMaxRows = 8;
+
+bool is_device_ptr(const void* p) {
+  if (p == nullptr) return false;
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static thread_local int cached_dev = -1, cached = 0;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached_dev = dev;
+    cached = n;
+  }
+  return cached;
+}
+
+}  // namespace gnf4
+
+using namespace gnf4;
+
+extern "C" {
+
+const char* gnf4_status_string(gnf4_status s) {
+  switch (s) {
+    case GNF4_OK: return "ok";
+    case GNF4_ERR_INVALID_ARG: return "invalid argument (null pointer, bad dimension or misalignment)";
+    case GNF4_ERR_NOT_DEVICE_PTR:
+      return "pointer is not device memory: libgnf4 runs on the GPU only; the CPU reference "
+             "computation is the oracle shipped with the tests, not a fallback";
+    case GNF4_ERR_UNSUPPORTED: return "size beyond the supported limits";
+    case GNF4_ERR_WORKSPACE: return "workspace missing or too small";
+    case GNF4_ERR_HIP: return "HIP runtime error (see gnf4_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int gnf4_last_hip_error(void) { return g_last_hip_error; }
+
+const char* gnf4_version(void) { return "0.1.0"; }
+
+gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
+                      uint8_t* packed, float* absmax, void* stream) {
+  if (!w || !packed || !absmax) return GNF4_ERR_INVALID_ARG;
+  if (E <= 0 || N <= 0 || K <= 0 || K % kBlock != 0) return GNF4_ERR_INVALID_ARG;
+  if (w_dtype != GNF4_DTYPE_BF16 && w_dtype != GNF4_DTYPE_F32) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(packed, 4) || !aligned(absmax, 4)) return GNF4_ERR_INVALID_ARG;
+  if (E > INT64_MAX / N || E * N > INT64_MAX / K) return GNF4_ERR_INVALID_ARG;
+  if (!is_device_ptr(w) || !is_device_ptr(packed) || !is_device_ptr(absmax))
+    return GNF4_ERR_NOT_DEVICE_PTR;
+  const int64_t n_blocks = E * N * (K / kBlock);
+  const hipError_t e = launch_pack(w, w_dtype, n_blocks, packed, absmax, (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+size_t gnf4_route_sort_workspace_size(int64_t T, int64_t E, int32_t top_k) {
+  if (T < 0 || E <= 0) return 0;
+  return plan_route(T, E, top_k).ws_bytes;
+}
+
+gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t top_k,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                            int32_t* sorted_slots, int32_t* group_sizes,
+                            int32_t* group_expert_ids, int32_t* num_groups, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (T < 0 || E <= 0 || top_k < 1 || top_k > E) return GNF4_ERR_INVALID_ARG;
+  if (E > 1024 || top_k > 32) return GNF4_ERR_UNSUPPORTED;
+  if (T > (int64_t)INT_MAX / top_k) return GNF4_ERR_UNSUPPORTED;
+  if (!expert_offsets || !group_sizes || !group_expert_ids || !num_groups)
+    return GNF4_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_slots)) return GNF4_ERR_INVALID_ARG;
+  const void* dev_ptrs[] = {expert_offsets, group_sizes, group_expert_ids, num_groups};
+  for (const void* p : dev_ptrs)
+    if (!aligned(p, 4)) return GNF4_ERR_INVALID_ARG;
+  if (T > 0) {
+    const void* more[] = {logits, topk_ids, topk_w, sorted_slots};
+    for (const void* p : more)
+      if (!aligned(p, 4)) return GNF4_ERR_INVALID_ARG;
+    for (const void* p : more)
+      if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  }
+  for (const void* p : dev_ptrs)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  const RoutePlan plan = plan_route(T, E, top_k);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return GNF4_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return GNF4_ERR_INVALID_ARG;
+    if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
+  }
+  const hipError_t e = launch_route_sort(logits, (int)T, (int)E, top_k, topk_ids, topk_w,
+                                         expert_offsets, sorted_slots, group_sizes,
+                                         group_expert_ids, num_groups,
+                                         static_cast<int32_t*>(workspace), plan,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const float* absmax,
+                               int64_t E, int64_t N, int64_t K, const int32_t* sizes,
+                               const int32_t* ids, int64_t G, int64_t M, uint16_t* y,
+                               void* ws, size_t ws_bytes, int32_t path, int32_t split_k,
+                               void* stream) {
+  if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
+    return GNF4_ERR_INVALID_ARG;
+  if (path < 0 || path > 2 || split_k < 0 || split_k > 16) return GNF4_ERR_INVALID_ARG;
+  if (M == 0 || G == 0) return GNF4_OK;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) ||
+      M * N >= ((int64_t)1 << 31) || E >= INT_MAX || G >= 65536)
+    return GNF4_ERR_UNSUPPORTED;
+  if (!x || !packed || !absmax || !sizes || !ids || !y) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(sizes, 4) ||
+      !aligned(ids, 4) || !aligned(y, 2))
+    return GNF4_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, packed, absmax, sizes, ids, y};
+  for (const void* p : ptrs)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+
+  GemmArgs a;
+  a.x = x;
+  a.packed = packed;
+  a.absmax = absmax;
+  a.sizes = sizes;
+  a.ids = ids;
+  a.y = y;
+  a.partial = nullptr;
+  a.E = (int)E;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)G;
+  a.M = (int)M;
+  bool run_decode = true, run_tile = true;
+  if (path == 1) {
+    a.rows_max_decode = INT_MAX;
+    a.rows_min_tile = INT_MAX;
+    run_tile = false;
+  } else if (path == 2) {
+    a.rows_max_decode = 0;
+    a.rows_min_tile = 1;
+    run_decode = false;
+  } else {
+    a.rows_max_decode = kDecodeMaxRows;
+    a.rows_min_tile = kDecodeMaxRows + 1;
+    // no group can exceed M rows: skip the tile launch when M is small
+    if (M <= kDecodeMaxRows) run_tile = false;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  if (run_decode) {
+    DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
+    const size_t need = decode_workspace_bytes(p, M, N);
+    if (need > 0) {
+      if (!ws || ws_bytes < need) {
+        if (split_k > 0) return GNF4_ERR_WORKSPACE;
+        p = plan_decode(M, N, K, G, 1, device_cu_count());  // no room to split: one pass
+      } else {
+        if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
+        if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
+        a.partial = static_cast<float*>(ws);
+      }
+    }
+    const hipError_t e = launch_decode(a, p, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (run_tile) {
+    const hipError_t e = launch_tile(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return GNF4_OK;
+}
+
+gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int32_t* sorted_slots,
+                             int32_t top_k, int64_t M, uint16_t* x_sorted, void* stream) {
+  if (T < 0 || M < 0 || top_k < 1 || K < kBlock || K % kBlock != 0) return GNF4_ERR_INVALID_ARG;
+  if (M == 0) return GNF4_OK;
+  if (T * top_k >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) || M >= ((int64_t)1 << 31))
+    return GNF4_ERR_UNSUPPORTED;
+  if (!x || !sorted_slots || !x_sorted) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_sorted, 16) || !aligned(sorted_slots, 4))
+    return GNF4_ERR_INVALID_ARG;
+  if (!is_device_ptr(x) || !is_device_ptr(sorted_slots) || !is_device_ptr(x_sorted))
+    return GNF4_ERR_NOT_DEVICE_PTR;
+  const hipError_t e = launch_gather(x, sorted_slots, top_k, (int)T, (int)M, (int)K, x_sorted,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
+                                           int64_t E, int32_t path, int32_t split_k) {
+  (void)E;
+  if (M <= 0 || N <= 0 || K < kBlock || G <= 0 || path == 2) return 0;
+  const DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
+  return decode_workspace_bytes(p, M, N);
+}
+
+size_t gnf4_grouped_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E) {
+  return gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, 0, 0);
+}
+
+gnf4_status gnf4_grouped_gemm(const uint16_t* x_sorted, const uint8_t* packed,
+                              const float* absmax, int64_t E, int64_t N, int64_t K,
+                              const int32_t* group_sizes, const int32_t* group_expert_ids,
+                              int64_t G, int64_t M, uint16_t* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return gemm_common(x_sorted, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
+                     workspace, workspace_bytes, 0, 0, stream);
+}
+
+gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed,
+                                 const float* absmax, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* group_sizes, const int32_t* group_expert_ids,
+                                 int64_t G, int64_t M, uint16_t* y, void* workspace,
+                                 size_t workspace_bytes, int32_t path, int32_t split_k,
+                                 void* stream) {
+  return gemm_common(x_sorted, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
+                     workspace, workspace_bytes, path, split_k, stream);
+}
+
+}  // extern "C"

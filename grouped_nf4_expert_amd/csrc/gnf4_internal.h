@@ -1,0 +1,108 @@
+// Internal declarations shared by the libgnf4 translation units.
+// Target: gfx950 (CDNA4) only: 64-lane wavefronts, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gnf4.h"
+
+namespace gnf4 {
+
+// NormalFloat4 levels (QLoRA, Dettmers et al. 2023, section 3), index = code.
+// The library's own copy of the spec constants.
+__host__ __device__ constexpr float nf4_level(int i) {
+  return i == 0 ? -1.0f
+       : i == 1 ? -0.6961928009986877f
+       : i == 2 ? -0.5250730514526367f
+       : i == 3 ? -0.39491748809814453f
+       : i == 4 ? -0.28444138169288635f
+       : i == 5 ? -0.18477343022823334f
+       : i == 6 ? -0.09105003625154495f
+       : i == 7 ? 0.0f
+       : i == 8 ? 0.07958029955625534f
+       : i == 9 ? 0.16093020141124725f
+       : i == 10 ? 0.2461123913526535f
+       : i == 11 ? 0.33791524171829224f
+       : i == 12 ? 0.44070982933044434f
+       : i == 13 ? 0.5626170039176941f
+       : i == 14 ? 0.7229568362236023f
+       : 1.0f;
+}
+
+constexpr int kBlock = 64;       // elements per absmax block along K
+constexpr int kZeroCode = 7;     // code of the exact zero level
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are validated by
+// the C-ABI layer before these are called.
+
+hipError_t launch_pack(const void* w, int dtype, int64_t n_blocks, uint8_t* packed,
+                       float* absmax, hipStream_t stream);
+
+struct RoutePlan {
+  int chunk_tokens;   // tokens per chunk of the sort
+  int n_chunks;       // 1 => single fused launch
+  size_t ws_bytes;    // per-chunk counts
+};
+RoutePlan plan_route(int64_t T, int64_t E, int top_k);
+
+hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                             int32_t* group_sizes, int32_t* group_expert_ids,
+                             int32_t* num_groups, int32_t* ws, const RoutePlan& plan,
+                             hipStream_t stream);
+
+struct GemmArgs {
+  const uint16_t* x;
+  const uint8_t* packed;
+  const float* absmax;
+  const int32_t* sizes;
+  const int32_t* ids;
+  uint16_t* y;
+  float* partial;     // split-K partials [S, M, N] (decode path)
+  int E, N, K, G, M;
+  int rows_max_decode;  // groups with size <= this take the decode path
+  int rows_min_tile;    // groups with size >= this take the tile path
+};
+
+struct DecodePlan {
+  int L;        // lanes per weight row (8, 16, 32, 64)
+  int NU;       // weight rows per lane
+  int S;        // K splits
+  int cps;      // 32-code chunks per split
+  int n_tiles;  // weight-row tiles per group
+  int rows_per_block;
+};
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, int num_cus);
+size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N);
+
+hipError_t launch_decode(const GemmArgs& a, const DecodePlan& p, hipStream_t stream);
+hipError_t launch_tile(const GemmArgs& a, hipStream_t stream);
+
+hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int T, int M, int K,
+                         uint16_t* out, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace gnf4

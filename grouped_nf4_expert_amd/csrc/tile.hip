@@ -1,0 +1,315 @@
+// Tile path of the grouped NF4 GEMM: groups with many rows (prefill), on the
+// CDNA4 matrix cores.
+//
+// Page "grouped-nf4-gemm -- single-launch W4A16 GEMM over fused NF4 MoE
+// expert stacks": "Layout" (the M-tile path) and "The claim" (prefill is the
+// compute-bound regime; the register-LUT mainloop decodes codes inside the
+// GEMM loop).  The pages' kernel was written for other hardware; this one is
+// built around gfx950's v_mfma_f32_32x32x16_f16.
+//
+// Precision: a single bf16 rounding of the decoded weights is too coarse for
+// an element-wise tolerance of 8e-3 |y| + 1e-3 rms(y) at K in the thousands,
+// while fp16 weights rounded ONCE from the fp32 product absmax * level are
+// well inside it.  So each weight row n gets a power-of-two scale 2^-s_n that
+// brings its largest block absmax into [0.5, 1); codes are decoded straight
+// to fp16(level * absmax * 2^-s_n) (fp32 product, one rounding), activations
+// are bf16 -> fp16 (exact inside the fp16 range), products accumulate in
+// fp32 on the matrix core, and the epilogue multiplies by 2^s_n exactly and
+// rounds to bf16.
+//
+// Work layout (XCD-aware): a workgroup of 4 wavefronts owns one (group, 256
+// output columns) tile and walks K in steps of 128 (two absmax blocks).  All
+// 4 wavefronts of one group's column tiles are dispatched to the same XCD so
+// the group's activation rows stay in that XCD's L2.  Each wavefront owns 64
+// columns (2 MFMA column tiles) for every row of the group (up to 6 row
+// tiles of 32 per pass), so every code is decoded exactly once per pass:
+//  * weights: a lane owns one weight row of each column tile and one 64-code
+//    absmax block per K step (lane half h = block h); it loads its 32 bytes
+//    straight from HBM into registers, builds the 16-entry fp16 table of that
+//    block (16 products, 8 packs, 8 byte-plane permutes) and decodes 8 codes
+//    per dword with v_perm_b32 byte lookups -- no LDS traffic for weights;
+//  * activations: the group's rows x 128 K of bf16 are staged through LDS as
+//    fp16 (double-buffered, rows padded to 272 bytes so the 16-byte fragment
+//    reads are bank-conflict-free) and stored in the same K order the weight
+//    decode produces, so A and B fragments agree slot by slot.
+
+#include "gnf4_internal.h"
+
+namespace gnf4 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kTileN = 256;        // output columns per workgroup
+constexpr int kStepK = 128;        // K per main-loop step
+constexpr int kRowTiles = 6;       // 32-row MFMA tiles per pass
+constexpr int kPassRows = 32 * kRowTiles;
+constexpr int kLdsRow = kStepK + 8;  // fp16 elements per staged row (padded)
+constexpr int kXChunks = kPassRows * (kStepK / 8) / kThreads;  // 16-byte loads per thread
+
+struct TileKArgs {
+  GemmArgs g;
+  int n_tiles;
+  int n_work;   // G * n_tiles
+};
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// fp16 decode table of one 64-code block: byte planes of fp16(level * a).
+struct Table {
+  uint32_t l0, l1, l2, l3, h0, h1, h2, h3;
+};
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ Table make_table(float a) {
+  uint32_t p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = pack_f16x2(nf4_level(2 * i) * a, nf4_level(2 * i + 1) * a);
+  Table t;
+  // low bytes of levels 4j..4j+3 and high bytes, from the packed pairs
+  t.l0 = perm(p[1], p[0], 0x06040200u);
+  t.h0 = perm(p[1], p[0], 0x07050301u);
+  t.l1 = perm(p[3], p[2], 0x06040200u);
+  t.h1 = perm(p[3], p[2], 0x07050301u);
+  t.l2 = perm(p[5], p[4], 0x06040200u);
+  t.h2 = perm(p[5], p[4], 0x07050301u);
+  t.l3 = perm(p[7], p[6], 0x06040200u);
+  t.h3 = perm(p[7], p[6], 0x07050301u);
+  return t;
+}
+
+// Four codes (one per byte of c, values 0..15) -> two dwords of fp16 pairs.
+// v_perm_b32 returns 0xff for a selector byte >= 13: codes 8..15 get selector
+// code+8 (16..23) in the low-half lookup and codes 0..7 get code+16 in the
+// high-half lookup, so AND-ing the two lookups keeps the valid byte.
+__device__ __forceinline__ void lookup4(uint32_t c, const Table& t, uint32_t& o0, uint32_t& o1) {
+  const uint32_t s_lo = c + (c & 0x08080808u);
+  const uint32_t s_hi = s_lo ^ 0x10101010u;
+  const uint32_t rl = perm(t.l1, t.l0, s_lo) & perm(t.l3, t.l2, s_hi);
+  const uint32_t rh = perm(t.h1, t.h0, s_lo) & perm(t.h3, t.h2, s_hi);
+  o0 = perm(rh, rl, 0x05010400u);
+  o1 = perm(rh, rl, 0x07030602u);
+}
+
+// Eight codes of one packed dword -> MFMA operand in the slot order
+// k = {0, 2, 4, 6, 1, 3, 5, 7} (high nibbles first).
+__device__ __forceinline__ half8 decode8(uint32_t d, const Table& t) {
+  uint32_t o[4];
+  lookup4((d >> 4) & 0x0f0f0f0fu, t, o[0], o[1]);
+  lookup4(d & 0x0f0f0f0fu, t, o[2], o[3]);
+  half8 r;
+  __builtin_memcpy(&r, o, sizeof(o));
+  return r;
+}
+
+// 8 bf16 (natural K order) -> 8 fp16 in the decode's slot order.  bf16 values
+// inside the fp16 range convert exactly, so round-toward-zero packing is
+// exact there (and clamps instead of overflowing outside it).
+__device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(d[j] << 16);
+    f[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+  }
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[2]));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[6]));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[1], f[3]));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[5], f[7]));
+  return r;
+}
+
+__device__ __forceinline__ int group_row_offset(const int32_t* sizes, int g, int lane) {
+  int sum = 0;
+  for (int i = lane; i < g; i += kWave) sum += max(sizes[i], 0);
+  return wave_sum(sum);
+}
+
+__global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
+  __shared__ int s_off;
+
+  // XCD-aware order: consecutive work items land on one XCD.
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int work = (b & 7) * (nb >> 3) + (b >> 3);
+  if (work >= a.n_work) return;
+  const int g = work / a.n_tiles;
+  const int nt = work % a.n_tiles;
+  const int sz = a.g.sizes[g];
+  const int e = a.g.ids[g];
+  if (sz < a.g.rows_min_tile || sz <= 0 || e < 0 || e >= a.g.E) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  if (tid < kWave) {
+    const int off = group_row_offset(a.g.sizes, g, tid);
+    if (tid == 0) s_off = off;
+  }
+  __syncthreads();
+  const int r_begin = s_off;
+  const int r_end = min(r_begin + sz, a.g.M);
+  if (r_begin >= r_end) return;
+
+  const int N = a.g.N, K = a.g.K;
+  const int i = lane & 31, h = lane >> 5;
+  const int n_wave = nt * kTileN + wave * 64;
+  const int nrow[2] = {n_wave + i, n_wave + 32 + i};
+  const size_t row_bytes = (size_t)K / 2;
+  const int bpr = K / kBlock;
+  const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
+  const float* aexp = a.g.absmax + (size_t)e * N * bpr;
+
+  // per-row power-of-two scale from the row's largest block absmax
+  int sexp[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float m = 0.0f;
+    if (nrow[t] < N) {
+      const float* ar = aexp + (size_t)nrow[t] * bpr;
+      for (int bk = h; bk < bpr; bk += 2) m = fmaxf(m, ar[bk]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    int ex = 0;
+    (void)frexpf(m, &ex);
+    sexp[t] = ex;
+  }
+
+  const int n_steps = K / kStepK;
+  const int rem_k = K - n_steps * kStepK;  // a final 64-wide step when K % 128 == 64
+
+  for (int p0 = r_begin; p0 < r_end; p0 += kPassRows) {
+    const int rows = min(kPassRows, r_end - p0);
+    const int rt_n = (rows + 31) / 32;
+
+    float16v acc[kRowTiles][2];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
+
+    const int total_steps = n_steps + (rem_k ? 1 : 0);
+
+    // x staging: thread owns 16-byte chunks q = tid + 256 * j of the pass
+    // tile (row q / 16, K slice 8 * (q % 16))
+    uint4 xr[kXChunks];
+    auto load_x = [&](int step) {
+      const int k0 = step * kStepK;
+#pragma unroll
+      for (int j = 0; j < kXChunks; ++j) {
+        const int q = tid + kThreads * j;
+        const int row = q >> 4, c16 = q & 15;
+        xr[j] = make_uint4(0, 0, 0, 0);
+        if (row < rows && k0 + 8 * c16 < K)
+          xr[j] = *reinterpret_cast<const uint4*>(a.g.x + (size_t)(p0 + row) * K + k0 + 8 * c16);
+      }
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < kXChunks; ++j) {
+        const int q = tid + kThreads * j;
+        const int row = q >> 4, c16 = q & 15;
+        if (row < rows)
+          *reinterpret_cast<uint4*>(&s_x[buf][row * kLdsRow + 8 * c16]) = bf16x8_to_f16_slots(xr[j]);
+      }
+    };
+    // weight codes: lane loads block h of its two rows for a step (32 bytes each)
+    uint4 wc[2][2];
+    float wa[2];
+    auto load_w = [&](int step) {
+      const int blk = 2 * step + h;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        wc[t][0] = wc[t][1] = make_uint4(0, 0, 0, 0);
+        wa[t] = 0.0f;
+        if (nrow[t] < N && blk < bpr) {
+          const uint4* p = reinterpret_cast<const uint4*>(wexp + (size_t)nrow[t] * row_bytes + 32 * (size_t)blk);
+          wc[t][0] = p[0];
+          wc[t][1] = p[1];
+          wa[t] = aexp[(size_t)nrow[t] * bpr + blk];
+        }
+      }
+    };
+
+    load_x(0);
+    load_w(0);
+    for (int step = 0; step < total_steps; ++step) {
+      const int buf = step & 1;
+      store_x(buf);
+      uint4 cw[2][2] = {{wc[0][0], wc[0][1]}, {wc[1][0], wc[1][1]}};
+      const float ca[2] = {wa[0], wa[1]};
+      __syncthreads();
+      if (step + 1 < total_steps) {
+        load_x(step + 1);
+        load_w(step + 1);
+      }
+      const Table tab0 = make_table(ldexpf(ca[0], -sexp[0]));
+      const Table tab1 = make_table(ldexpf(ca[1], -sexp[1]));
+      const bool half_step = (rem_k != 0) && (step == n_steps);  // only block 0 valid
+      const _Float16* xs = &s_x[buf][0];
+#pragma unroll
+      for (int sub = 0; sub < 8; ++sub) {
+        const uint32_t d0 = (&cw[0][0].x)[sub];
+        const uint32_t d1 = (&cw[1][0].x)[sub];
+        half8 bw0 = decode8(d0, tab0);
+        half8 bw1 = decode8(d1, tab1);
+        if (half_step && h) {  // lanes of the missing block contribute zero
+          bw0 = (half8){};
+          bw1 = (half8){};
+        }
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) {
+          if (rt < rt_n) {
+            const half8 ax = *reinterpret_cast<const half8*>(xs + (rt * 32 + i) * kLdsRow + 64 * h + 8 * sub);
+            acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bw0, acc[rt][0], 0, 0, 0);
+            acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bw1, acc[rt][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // epilogue: D[row][col], col = lane % 32, row = 8 (v / 4) + 4 h + v % 4
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      if (rt >= rt_n) continue;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int n = nrow[t];
+        if (n >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = p0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (row < r_end) a.g.y[(size_t)row * N + n] = f32_to_bf16(ldexpf(acc[rt][t][v], sexp[t]));
+        }
+      }
+    }
+    __syncthreads();  // the next pass reuses the LDS buffers
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
+  TileKArgs a;
+  a.g = g;
+  a.n_tiles = (g.N + kTileN - 1) / kTileN;
+  a.n_work = g.G * a.n_tiles;
+  const int grid = ((a.n_work + 7) / 8) * 8;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gnf4

@@ -1,0 +1,226 @@
+"""Thin Python binding over libgnf4 (include/gnf4.h).
+
+Argument marshalling only: tensors are checked for dtype, shape and device,
+their data pointers and the current HIP stream are handed to the C ABI, and
+output tensors are allocated with torch (torch is used for device memory and
+streams, nothing else).  Every computation happens in the library's HIP
+kernels.  The library must be built (``python -m grouped_nf4_expert_amd.build``);
+if it is missing, or a tensor is not on the GPU, the call raises -- there is
+no CPU path and no fallback.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgnf4.so")
+
+GNF4_OK = 0
+GNF4_DTYPE_BF16 = 0
+GNF4_DTYPE_F32 = 1
+PATH_AUTO, PATH_DECODE, PATH_TILE = 0, 1, 2
+
+_lib = None
+
+
+class Gnf4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        text = library().gnf4_status_string(status).decode()
+        extra = ""
+        if status == 5:
+            extra = f" (hipError {library().gnf4_last_hip_error()})"
+        super().__init__(f"{where}: {text}{extra}")
+
+
+def library():
+    """Load libgnf4.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m grouped_nf4_expert_amd.build` "
+            "(the grouped NF4 GEMM has no CPU implementation to fall back to)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.gnf4_status_string.restype = ctypes.c_char_p
+    lib.gnf4_status_string.argtypes = [ctypes.c_int]
+    lib.gnf4_last_hip_error.restype = ctypes.c_int
+    lib.gnf4_last_hip_error.argtypes = []
+    lib.gnf4_version.restype = ctypes.c_char_p
+    lib.gnf4_version.argtypes = []
+    lib.gnf4_pack.restype = ctypes.c_int
+    lib.gnf4_pack.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.gnf4_route_sort_workspace_size.restype = sz
+    lib.gnf4_route_sort_workspace_size.argtypes = [i64, i64, i32]
+    lib.gnf4_route_sort.restype = ctypes.c_int
+    lib.gnf4_route_sort.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gnf4_gather_rows.restype = ctypes.c_int
+    lib.gnf4_gather_rows.argtypes = [vp, i64, i64, vp, i32, i64, vp, vp]
+    lib.gnf4_grouped_gemm_workspace_size.restype = sz
+    lib.gnf4_grouped_gemm_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.gnf4_grouped_gemm_workspace_size_ex.restype = sz
+    lib.gnf4_grouped_gemm_workspace_size_ex.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.gnf4_grouped_gemm.restype = ctypes.c_int
+    lib.gnf4_grouped_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz, vp]
+    lib.gnf4_grouped_gemm_ex.restype = ctypes.c_int
+    lib.gnf4_grouped_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp,
+                                         sz, i32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check(status, where):
+    if status != GNF4_OK:
+        raise Gnf4Error(status, where)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------- pack
+
+def pack(w, out=None):
+    """NF4-pack ``w`` [..., N, K] (bf16 or fp32 on the GPU).
+
+    Returns ``(packed uint8 [..., N, K/2], absmax fp32 [..., N, K/64])``.
+    """
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("w must be bfloat16 or float32")
+    _need(w, "w", w.dtype)
+    if w.dim() < 2:
+        raise ValueError("w must be at least 2-D")
+    K = w.shape[-1]
+    N = w.shape[-2]
+    E = w.numel() // max(N * K, 1)
+    if out is None:
+        packed = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+        absmax = torch.empty(w.shape[:-1] + (K // 64,), dtype=torch.float32, device=w.device)
+    else:
+        packed, absmax = out
+    dt = GNF4_DTYPE_BF16 if w.dtype == torch.bfloat16 else GNF4_DTYPE_F32
+    _check(library().gnf4_pack(_ptr(w), dt, E, N, K, _ptr(packed), _ptr(absmax), _stream()),
+           "gnf4_pack")
+    return packed, absmax
+
+
+# ------------------------------------------------------------- route_sort
+
+@dataclass
+class RouteResult:
+    topk_ids: torch.Tensor        # int32 [T, k]
+    topk_w: torch.Tensor          # fp32 [T, k]
+    expert_offsets: torch.Tensor  # int32 [E + 1]
+    sorted_slots: torch.Tensor    # int32 [T * k]
+    group_sizes: torch.Tensor     # int32 [E]
+    group_expert_ids: torch.Tensor  # int32 [E]
+    num_groups: torch.Tensor      # int32 [1]
+
+
+class RouteBuffers:
+    """Preallocated outputs and workspace for repeated route_sort calls."""
+
+    def __init__(self, T, E, top_k, device):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.T, self.E, self.top_k = T, E, top_k
+        self.result = RouteResult(
+            topk_ids=torch.empty((T, top_k), **i32),
+            topk_w=torch.empty((T, top_k), dtype=torch.float32, device=device),
+            expert_offsets=torch.empty(E + 1, **i32),
+            sorted_slots=torch.empty(T * top_k, **i32),
+            group_sizes=torch.empty(E, **i32),
+            group_expert_ids=torch.empty(E, **i32),
+            num_groups=torch.empty(1, **i32),
+        )
+        nbytes = library().gnf4_route_sort_workspace_size(T, E, top_k)
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        self.ws_bytes = nbytes
+
+
+def route_sort(logits, top_k, buffers=None):
+    """Top-k routing with softmax weights and the stable token->expert sort."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if buffers is None:
+        buffers = RouteBuffers(T, E, top_k, logits.device)
+    r = buffers.result
+    _check(library().gnf4_route_sort(
+        _ptr(logits), T, E, top_k, _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.expert_offsets),
+        _ptr(r.sorted_slots), _ptr(r.group_sizes), _ptr(r.group_expert_ids),
+        _ptr(r.num_groups), _ptr(buffers.workspace), buffers.ws_bytes, _stream()),
+        "gnf4_route_sort")
+    return r
+
+
+# ------------------------------------------------------------ gather_rows
+
+def gather_rows(x, sorted_slots, top_k, out=None):
+    """x_sorted[r] = x[sorted_slots[r] // top_k] (bf16 rows)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(sorted_slots, "sorted_slots", torch.int32, 1)
+    T, K = x.shape
+    M = sorted_slots.numel()
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _check(library().gnf4_gather_rows(_ptr(x), T, K, _ptr(sorted_slots), top_k, M, _ptr(out),
+                                      _stream()), "gnf4_gather_rows")
+    return out
+
+
+# ----------------------------------------------------------- grouped_gemm
+
+def gemm_workspace_size(M, N, K, G, E, path=PATH_AUTO, split_k=0):
+    return library().gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, path, split_k)
+
+
+def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None, y=None,
+                 workspace=None, path=PATH_AUTO, split_k=0):
+    """y[M, N] (bf16) = per-group x_sorted[rows] @ dequant(W[expert])^T.
+
+    ``G`` defaults to ``min(len(group_sizes), M)``, which is exact for the
+    compact groups route_sort emits (non-empty groups come first).
+    """
+    _need(x_sorted, "x_sorted", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(absmax, "absmax", torch.float32, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
+    M, K = x_sorted.shape
+    E, N, half_k = packed.shape
+    if half_k * 2 != K or absmax.shape != (E, N, K // 64):
+        raise ValueError("packed/absmax shapes do not match x_sorted's K")
+    if G is None:
+        G = min(group_sizes.numel(), M)
+    if G > group_sizes.numel() or G > group_expert_ids.numel():
+        raise ValueError("G exceeds the group arrays")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x_sorted.device)
+    need = gemm_workspace_size(M, N, K, G, E, path, split_k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_sorted.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gnf4_grouped_gemm_ex(
+        _ptr(x_sorted), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes),
+        _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes, path, split_k,
+        _stream()), "gnf4_grouped_gemm")
+    return y

@@ -1,0 +1,217 @@
+/*
+ * gnf4.h -- C ABI of libgnf4: the grouped Mixture-of-Experts expert GEMM
+ * (W4A16) computed directly on NF4-packed expert weights, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed (page "grouped-nf4-gemm -- single-launch W4A16 GEMM over
+ * fused NF4 MoE expert stacks", opening section): a stack of E expert weight
+ * matrices, each [N, K], stored as NF4 -- an [E, N, K/2] uint8 array holding
+ * two 4-bit codes per byte plus one fp32 absmax per 64-element block along K
+ * -- is multiplied by bf16 activations that a token->expert sort has grouped
+ * by expert and described with (sizes, expert_ids).  Every code is decoded
+ * through the 16-entry NormalFloat4 table, scaled by its block absmax,
+ * accumulated in fp32 and stored as bf16, in one launch for all active
+ * experts; no dequantised copy of the weights is ever written.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers (memory from hipMalloc or a caching
+ *    allocator built on it) unless stated otherwise.  A host pointer is
+ *    refused with GNF4_ERR_NOT_DEVICE_PTR: there is no CPU path and nothing
+ *    falls back silently (landing page "grouped-nf4-gemm", "Do not use this
+ *    when": the grouped GEMM refuses CPU tensors).  The reference computation
+ *    on the CPU is the oracle that ships with the tests, not this library.
+ *  - bf16 values travel as their raw 16-bit patterns (uint16_t).
+ *  - Arrays are dense and row-major.  Vector-loaded inputs (weights,
+ *    activations, packed codes) must be 16-byte aligned; others 4-byte.
+ *  - The caller owns every buffer, including workspace.  The library keeps
+ *    no per-call state and never synchronises the host: each call enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns.  Results are valid once the stream has completed them.
+ *  - Outputs must not alias inputs.  Calls on different streams may run
+ *    concurrently; calls sharing a workspace must be ordered by the caller.
+ *  - Status codes report host-checkable misuse synchronously.  Values that
+ *    live on the device (group sizes, expert ids) are not read by the host:
+ *    kernels skip a group whose size is <= 0 or whose expert id is outside
+ *    [0, E), and never touch rows at or beyond M.
+ */
+#ifndef GNF4_H_
+#define GNF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gnf4_status {
+  GNF4_OK = 0,
+  GNF4_ERR_INVALID_ARG = 1,     /* null pointer, bad dimension, misalignment */
+  GNF4_ERR_NOT_DEVICE_PTR = 2,  /* a pointer is not device memory */
+  GNF4_ERR_UNSUPPORTED = 3,     /* a size beyond what the kernels support */
+  GNF4_ERR_WORKSPACE = 4,       /* workspace missing or too small */
+  GNF4_ERR_HIP = 5              /* a HIP runtime call failed; see gnf4_last_hip_error */
+} gnf4_status;
+
+typedef enum gnf4_dtype {
+  GNF4_DTYPE_BF16 = 0,
+  GNF4_DTYPE_F32 = 1
+} gnf4_dtype;
+
+/* Human-readable text for a status code (static storage). */
+const char* gnf4_status_string(gnf4_status s);
+
+/* hipError_t of the most recent GNF4_ERR_HIP returned on this host thread. */
+int gnf4_last_hip_error(void);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* gnf4_version(void);
+
+/*
+ * gnf4_pack -- blockwise NF4 quantisation of an expert weight stack.
+ *
+ * Page "grouped-nf4-gemm -- single-launch W4A16 GEMM ...", opening section
+ * (the [E, N, K/2] uint8 + fp32 blockwise absmax layout of the bitsandbytes
+ * gemm_4bit family); "Cross-vendor projections" (3.56x smaller than bf16,
+ * i.e. one fp32 absmax per 64 codes).  Code values: QLoRA (Dettmers et al.,
+ * 2023), section 3, NormalFloat4.
+ *
+ *   w       [E, N, K] of `w_dtype` (bf16 bits or fp32), 16-byte aligned
+ *   packed  [E, N, K/2] uint8 out: byte j of a row = (code[2j] << 4) | code[2j+1]
+ *           (first element in the high nibble), 4-byte aligned
+ *   absmax  [E, N, K/64] fp32 out: max |w| over each 64-element block
+ *
+ * For each block with absmax a > 0, the code of x is the index of the table
+ * level nearest to x / a in exact arithmetic, ties to the lower index (the
+ * comparison x > m_i * a against level midpoints m_i is done in fp64, where
+ * it is exact).  A block with a == 0 stores code 7 (the exact zero level)
+ * everywhere.  Inputs must be finite.  K must be a positive multiple of 64.
+ * Errors: GNF4_ERR_INVALID_ARG (null pointer, E/N/K <= 0, K % 64 != 0, bad
+ * dtype, misalignment), GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_HIP.
+ */
+gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
+                      uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * gnf4_route_sort -- router top-k with softmax weights, then the
+ * token->expert sort that yields (sizes, expert_ids).
+ *
+ * Page "grouped-nf4-gemm -- single-launch W4A16 GEMM ...", opening section
+ * ("(sizes, expert_ids) supplied after the usual token->expert sort");
+ * landing page "grouped-nf4-gemm", "Use this when" (router softmax and
+ * top-k as one decode-step glue launch).
+ *
+ *   logits            [T, E] fp32 router logits (finite; NaN is outside the contract)
+ *   topk_ids          [T, top_k] int32 out: the top_k experts of each token,
+ *                     by descending logit, equal logits to the lower id
+ *   topk_w            [T, top_k] fp32 out: softmax over the top_k selected logits
+ *   expert_offsets    [E + 1] int32 out: exclusive prefix sum of rows per expert
+ *   sorted_slots      [T * top_k] int32 out: flat slots s = t * top_k + j grouped
+ *                     by ascending expert id, ascending s inside an expert
+ *                     (stable; row r of the grouped activations is token
+ *                     sorted_slots[r] / top_k)
+ *   group_sizes       [E] int32 out: rows of each non-empty expert, in
+ *                     ascending expert id; the tail after num_groups is zero
+ *   group_expert_ids  [E] int32 out: the matching expert ids; tail zero
+ *   num_groups        [1] int32 out: number of non-empty experts
+ *   workspace         device scratch of gnf4_route_sort_workspace_size() bytes
+ *                     (may be NULL when that size is 0)
+ *
+ * Limits: 0 <= T, 1 <= E <= 1024, 1 <= top_k <= min(E, 32).  T == 0 writes
+ * zero offsets and zero groups.  Bit-exact, deterministic (no atomics decide
+ * an order).  Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_UNSUPPORTED (E or top_k
+ * above the limits), GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE, GNF4_ERR_HIP.
+ */
+size_t gnf4_route_sort_workspace_size(int64_t T, int64_t E, int32_t top_k);
+
+gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t top_k,
+                            int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                            int32_t* sorted_slots, int32_t* group_sizes,
+                            int32_t* group_expert_ids, int32_t* num_groups,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gnf4_gather_rows -- build the grouped activations from token rows:
+ * x_sorted[r, :] = x[sorted_slots[r] / top_k, :] for r < M.
+ *
+ * Page "grouped-nf4-gemm -- single-launch W4A16 GEMM ...", opening section:
+ * the GEMM consumes activations already grouped by the token->expert sort.
+ *
+ *   x             [T, K] bf16 bits (token activations), 16-byte aligned
+ *   sorted_slots  [M] int32 flat slots as gnf4_route_sort writes them
+ *   x_sorted      [M, K] bf16 bits out, 16-byte aligned
+ *
+ * A slot outside [0, T * top_k) leaves its row untouched.  K must be a
+ * positive multiple of 64.  Errors: GNF4_ERR_INVALID_ARG,
+ * GNF4_ERR_UNSUPPORTED, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_HIP.
+ */
+gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int32_t* sorted_slots,
+                             int32_t top_k, int64_t M, uint16_t* x_sorted, void* stream);
+
+/*
+ * gnf4_grouped_gemm -- y = x_sorted . dequant(W[expert_ids[g]])^T per group,
+ * every active expert in one pass.
+ *
+ * Page "grouped-nf4-gemm -- single-launch W4A16 GEMM ...", opening section
+ * and "The claim" (LUT decode, blockwise fp32 absmax, fp32 accumulation,
+ * bf16 epilogue, one launch for all active experts); "Layout" (a decode GEMV
+ * path and an M-tile path); "Status / roadmap" (split-K for starved grids,
+ * one universal launch rule instead of per-shape tables).
+ *
+ *   x_sorted          [M, K] bf16 bits, rows grouped by expert, 16-byte aligned
+ *   packed, absmax    [E, N, K/2] uint8 and [E, N, K/64] fp32 (as gnf4_pack writes)
+ *   group_sizes       [G] int32: rows of group g (contiguous, in group order)
+ *   group_expert_ids  [G] int32: expert of group g (duplicates allowed)
+ *   y                 [M, N] bf16 bits out; only rows covered by a valid group
+ *                     are written, the rest keep their contents
+ *   workspace         device scratch of gnf4_grouped_gemm_workspace_size() bytes
+ *
+ * Group g covers rows [sum_{g'<g} max(size_g', 0), + size_g) clipped to M.
+ * Routing weights are not applied here (the top-k combine is separate glue).
+ * Two kernels implement the same arithmetic contract: a bandwidth-bound
+ * decode path for groups with few rows (fp32 decode and multiply-add, optional
+ * split-K with a fixed-order fp32 reduce) and a matrix-core tile path for
+ * groups with many rows (per-row power-of-two scaling, codes decoded with
+ * their block absmax into fp16, fp16 x fp16 -> fp32 MFMA).  Which one runs
+ * is a performance choice made from host-known sizes only; both meet
+ * |y - exact| <= 8e-3 |exact| + 1e-3 rms(exact) per element for activations
+ * within the fp16 range (|x| <= 65504) on the tile path.  Results are
+ * deterministic run to run.
+ *
+ * Limits: M >= 0, G >= 0 (either 0: nothing to do), E, N >= 1, K >= 64 with
+ * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call.
+ * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE,
+ * GNF4_ERR_HIP.
+ */
+size_t gnf4_grouped_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);
+
+gnf4_status gnf4_grouped_gemm(const uint16_t* x_sorted, const uint8_t* packed,
+                              const float* absmax, int64_t E, int64_t N, int64_t K,
+                              const int32_t* group_sizes, const int32_t* group_expert_ids,
+                              int64_t G, int64_t M, uint16_t* y,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gnf4_grouped_gemm_ex -- gnf4_grouped_gemm with the path choice exposed, for
+ * tests and tuning.  `path`: 0 = automatic (same as gnf4_grouped_gemm),
+ * 1 = every group on the decode path, 2 = every group on the tile path.
+ * `split_k`: 0 = automatic, else the number of K splits of the decode path
+ * (1..16; needs workspace of gnf4_grouped_gemm_workspace_size_ex()).
+ * Results of all paths satisfy the same tolerance contract.
+ */
+size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
+                                           int64_t E, int32_t path, int32_t split_k);
+
+gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed,
+                                 const float* absmax, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* group_sizes, const int32_t* group_expert_ids,
+                                 int64_t G, int64_t M, uint16_t* y,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t path, int32_t split_k, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* GNF4_H_ */

@@ -1,0 +1,113 @@
+"""The C-ABI library loads and exports every symbol include/gnf4.h declares.
+
+CPU only: no kernel is launched.  Host-checkable misuse (null pointers, bad
+dimensions, unsupported sizes) is rejected before any HIP call, so those
+status codes are checked here as well.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from grouped_nf4_expert_amd import gnf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gnf4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gnf4_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gnf4.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gnf4.library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gnf4_pack", "gnf4_route_sort", "gnf4_grouped_gemm", "gnf4_gather_rows"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", gnf4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gnf4_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.gnf4_status_string(s)
+    assert b"oracle" in lib.gnf4_status_string(2)
+    assert lib.gnf4_version() == b"0.1.0"
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "gnf4.h"\nint main(void){return (int)GNF4_OK;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    "-c", str(src), "-o", str(tmp_path / "t.o")], check=True)
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: rejected before any HIP call
+
+
+def test_pack_rejects_bad_arguments(lib):
+    assert lib.gnf4_pack(NULL, 0, 1, 1, 64, FAKE, FAKE, NULL) == 1
+    assert lib.gnf4_pack(FAKE, 0, 1, 1, 96, FAKE, FAKE, NULL) == 1     # K % 64
+    assert lib.gnf4_pack(FAKE, 0, 0, 1, 64, FAKE, FAKE, NULL) == 1     # E <= 0
+    assert lib.gnf4_pack(FAKE, 7, 1, 1, 64, FAKE, FAKE, NULL) == 1     # dtype
+    assert lib.gnf4_pack(ctypes.c_void_p(0x1008), 0, 1, 1, 64, FAKE, FAKE, NULL) == 1  # align
+
+
+def test_route_rejects_bad_arguments(lib):
+    args = [FAKE] * 7 + [NULL, 0, NULL]
+    assert lib.gnf4_route_sort(FAKE, 4, 8, 0, *args) == 1        # top_k < 1
+    assert lib.gnf4_route_sort(FAKE, 4, 8, 9, *args) == 1        # top_k > E
+    assert lib.gnf4_route_sort(FAKE, 4, 2048, 8, *args) == 3     # E > 1024
+    assert lib.gnf4_route_sort(FAKE, 4, 64, 33, *args) == 3      # top_k > 32
+    assert lib.gnf4_route_sort(FAKE, -1, 8, 2, *args) == 1       # T < 0
+    assert lib.gnf4_route_sort(NULL, 4, 8, 2, *args) == 1        # null logits
+
+
+def test_gemm_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(x=FAKE, p=FAKE, a=FAKE, E=4, N=64, K=128, s=FAKE, i=FAKE, G=2, M=8, y=FAKE,
+                 path=0, split=0)
+        a.update(kw)
+        return lib.gnf4_grouped_gemm_ex(a["x"], a["p"], a["a"], a["E"], a["N"], a["K"], a["s"],
+                                        a["i"], a["G"], a["M"], a["y"], NULL, 0, a["path"],
+                                        a["split"], NULL)
+    assert call(K=96) == 1
+    assert call(K=32) == 1
+    assert call(N=0) == 1
+    assert call(M=-1) == 1
+    assert call(path=3) == 1
+    assert call(split=17) == 1
+    assert call(x=NULL) == 1
+    assert call(M=0) == 0     # nothing to do
+    assert call(G=0) == 0
+    assert call(x=ctypes.c_void_p(0x1004)) == 1   # x must be 16-byte aligned
+    assert lib.gnf4_gather_rows(FAKE, 4, 96, FAKE, 2, 8, FAKE, NULL) == 1
+
+
+def test_no_cpu_fallback_in_binding():
+    """The binding never routes through the oracle or a torch fallback."""
+    src = open(os.path.join(ROOT, "grouped_nf4_expert_amd", "gnf4.py")).read()
+    assert "oracle" not in src
+    for line in src.splitlines():
+        assert "import numpy" not in line
