@@ -1,0 +1,365 @@
+"""Benchmark of the grouped NF4 expert GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload olmoe]
+                    [--cells cells.jsonl] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: for each of L MoE
+layers (distinct weights and router logits, all resident in HBM),
+route/sort -> gate_up grouped GEMM (reading token rows through the sort:
+the row gather is fused) -> down grouped GEMM,
+every step in libgnf4's kernels.  Weights are packed once beforehand (the
+pages quantise at bake time).  L is chosen so the step's expert bytes
+exceed the 256 MB Infinity Cache, so each layer's weights stream from HBM.
+
+Printed: ONE JSON line with the effective HBM throughput of the step
+(algorithmic bytes / step time), the roofline of the dominant kernel
+(average launch duration from HIP events recorded around each of its
+launches inside the timed region), and the CPU oracle's throughput on a
+bounded sample of the same workload.  --cells additionally measures every
+workload's GEMMs alone (decode GB/s, prefill TFLOP/s) into a JSONL file.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+METRIC = "grouped NF4 GEMM effective HBM GB/s (decode) & TFLOP/s (prefill), % roofline"
+
+
+def gemm_bytes(n_touched, M, N, K):
+    """Algorithmic bytes of one grouped GEMM: each touched expert's codes and
+    absmax once, the activations read once, the output written once."""
+    return n_touched * (N * K // 2 + 4 * N * K // 64) + 2 * M * K + 2 * M * N
+
+
+def route_bytes(T, E, k):
+    M = T * k
+    return 4 * T * E + 8 * T * k + 4 * (E + 1) + 4 * M + 8 * E + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe")
+    ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
+    ap.add_argument("--cells", default="", help="also time every workload's GEMMs into this JSONL")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch every kernel from the host instead of replaying a HIP graph")
+    return ap.parse_args()
+
+
+class Layer:
+    pass
+
+
+def capture(fn):
+    """Record fn's launches (all on the current stream) into a HIP graph."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def build_layers(wl, L, dev):
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+
+    Kg, Ng = wl.gemm("gate_up")
+    Kd, Nd = wl.gemm("down")
+    layers = []
+    for li in range(L):
+        ly = Layer()
+        ly.pg = torch.empty((wl.E, Ng, Kg // 2), dtype=torch.uint8, device=dev)
+        ly.ag = torch.empty((wl.E, Ng, Kg // 64), dtype=torch.float32, device=dev)
+        ly.pd = torch.empty((wl.E, Nd, Kd // 2), dtype=torch.uint8, device=dev)
+        ly.ad = torch.empty((wl.E, Nd, Kd // 64), dtype=torch.float32, device=dev)
+        for e in range(wl.E):
+            gnf4.pack(wls.expert_weights_device(wl, "gate_up", e, dev, li), out=(ly.pg[e], ly.ag[e]))
+            gnf4.pack(wls.expert_weights_device(wl, "down", e, dev, li), out=(ly.pd[e], ly.ad[e]))
+        ly.logits = torch.from_numpy(wls.router_logits(wl, li)).to(dev)
+        ly.x = wls.activations_device(wl.T, Kg, dev, wl.seed, 21, li)
+        ly.xd = wls.activations_device(wl.M, Kd, dev, wl.seed, 22, li)
+        ly.route = gnf4.RouteBuffers(wl.T, wl.E, wl.top_k, dev)
+        ly.xs = torch.empty((wl.M, Kg), dtype=torch.bfloat16, device=dev)
+        ly.yg = torch.empty((wl.M, Ng), dtype=torch.bfloat16, device=dev)
+        ly.yd = torch.empty((wl.M, Nd), dtype=torch.bfloat16, device=dev)
+        G = min(wl.E, wl.M)
+        ly.G = G
+        wsg = gnf4.gemm_workspace_size(wl.M, Ng, Kg, G, wl.E)
+        wsd = gnf4.gemm_workspace_size(wl.M, Nd, Kd, G, wl.E)
+        ly.wsg = torch.empty(max(wsg, 16), dtype=torch.uint8, device=dev)
+        ly.wsd = torch.empty(max(wsd, 16), dtype=torch.uint8, device=dev)
+        layers.append(ly)
+    torch.cuda.synchronize()
+    return layers
+
+
+def gate_up(wl, ly):
+    """gate_up GEMM reading the token rows through the sort (fused gather)."""
+    from grouped_nf4_expert_amd import gnf4
+    r = ly.route.result
+    gnf4.grouped_gemm(ly.x, ly.pg, ly.ag, r.group_sizes, r.group_expert_ids, G=ly.G, y=ly.yg,
+                      workspace=ly.wsg, sorted_slots=r.sorted_slots, top_k=wl.top_k)
+
+
+def run_layer(wl, ly):
+    from grouped_nf4_expert_amd import gnf4
+    r = gnf4.route_sort(ly.logits, wl.top_k, ly.route)
+    gate_up(wl, ly)
+    gnf4.grouped_gemm(ly.xd, ly.pd, ly.ad, r.group_sizes, r.group_expert_ids, G=ly.G, y=ly.yd,
+                      workspace=ly.wsd)
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands, on one layer of the same workload, repeated
+    until about `seconds` of CPU time have passed."""
+    import oracle
+    from grouped_nf4_expert_amd import workloads as wls
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    Kg, Ng = wl.gemm("gate_up")
+    Kd, Nd = wl.gemm("down")
+    logits = wls.router_logits(wl, 0)
+    rr = oracle.ref_route_sort(logits, wl.top_k)
+    used = rr["group_expert_ids"][: rr["num_groups"]]
+    pg = np.zeros((wl.E, Ng, Kg // 2), np.uint8)
+    ag = np.zeros((wl.E, Ng, Kg // 64), np.float32)
+    pd = np.zeros((wl.E, Nd, Kd // 2), np.uint8)
+    ad = np.zeros((wl.E, Nd, Kd // 64), np.float32)
+    for e in used:
+        pg[e], ag[e] = oracle.ref_pack(wls.expert_weights(wl, "gate_up", int(e)))
+        pd[e], ad[e] = oracle.ref_pack(wls.expert_weights(wl, "down", int(e)))
+    x_tok = wls.token_activations(wl, Kg)
+    xd = wls.down_input(wl, wl.M, Kd)
+    n = len(used)
+    layer_bytes = (route_bytes(wl.T, wl.E, wl.top_k) +
+                   gemm_bytes(n, wl.M, Ng, Kg) + gemm_bytes(n, wl.M, Nd, Kd))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        r = oracle.ref_route_sort(logits, wl.top_k)
+        xs = x_tok[r["sorted_slots"] // wl.top_k]
+        oracle.ref_grouped_gemm(xs, pg, ag, r["group_sizes"], r["group_expert_ids"])
+        oracle.ref_grouped_gemm(xd, pd, ad, r["group_sizes"], r["group_expert_ids"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(layer_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} x one {wl.name} layer (route+sort, gather, gate_up + down GEMM over "
+                      f"{n} touched experts) in {el:.1f} s; fp64 numpy, BLAS threads={threads}"}
+
+
+def time_cells(path, dev):
+    """Each workload's GEMMs alone, cycling over enough weight copies to
+    defeat the Infinity Cache; per-launch HIP events."""
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    out = open(path, "w")
+    for name in ("olmoe", "qwen3_t1", "qwen3_t8", "gptoss", "dsv3"):
+        wl = wls.WORKLOADS[name]
+        lg = torch.from_numpy(wls.router_logits(wl)).to(dev)
+        r = gnf4.route_sort(lg, wl.top_k)
+        G = min(wl.E, wl.M)
+        ng = int(r.num_groups.cpu()[0])
+        for gemm in ("gate_up", "down"):
+            K, N = wl.gemm(gemm)
+            stack_bytes = wl.E * (N * K // 2 + N * K // 16)
+            copies = max(1, min(8, int(np.ceil(600e6 / stack_bytes))))
+            stacks = []
+            for ci in range(copies):
+                p = torch.empty((wl.E, N, K // 2), dtype=torch.uint8, device=dev)
+                a = torch.empty((wl.E, N, K // 64), dtype=torch.float32, device=dev)
+                for e in range(wl.E):
+                    gnf4.pack(wls.expert_weights_device(wl, gemm, e, dev, 100 + ci), out=(p[e], a[e]))
+                stacks.append((p, a))
+            x = wls.activations_device(wl.M, K, dev, wl.seed, 50, K)
+            y = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(gnf4.gemm_workspace_size(wl.M, N, K, G, wl.E), 16),
+                             dtype=torch.uint8, device=dev)
+            per = 4 * copies if name != "dsv3" else copies
+
+            def launches():
+                for i in range(per):
+                    p, a = stacks[i % copies]
+                    gnf4.grouped_gemm(x, p, a, r.group_sizes, r.group_expert_ids, G=G, y=y,
+                                      workspace=ws)
+            graph = capture(launches)
+            reps = 10 if name != "dsv3" else 3
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            graph.replay()
+            torch.cuda.synchronize()
+            for i in range(reps):
+                evs[i][0].record()
+                graph.replay()
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            us = sorted(s.elapsed_time(e) * 1e3 / per for s, e in evs)
+            med = us[len(us) // 2]
+            byt = gemm_bytes(ng, wl.M, N, K)
+            flops = 2.0 * wl.M * N * K
+            rec = {"workload": name, "gemm": gemm, "E": wl.E, "top_k": wl.top_k, "T": wl.T,
+                   "M": wl.M, "K": K, "N": N, "touched_experts": ng, "median_us": round(med, 2),
+                   "min_us": round(us[0], 2), "GBps": round(byt / med / 1e3, 1),
+                   "TFLOPs": round(flops / med / 1e6, 2),
+                   "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
+                   "mfma_frac": round(flops / med / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4),
+                   "weight_copies": copies}
+            out.write(json.dumps(rec) + "\n")
+            out.flush()
+            print(f"[cell] {json.dumps(rec)}", file=sys.stderr, flush=True)
+            del stacks
+            torch.cuda.empty_cache()
+    out.close()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gnf4.library()
+    dev = torch.device("cuda:0")
+    wl = wls.WORKLOADS[args.workload]
+    L = args.layers or wl.layers
+    print(f"[bench] building {L} layers of {wl.name}", file=sys.stderr, flush=True)
+    layers = build_layers(wl, L, dev)
+
+    Kg, Ng = wl.gemm("gate_up")
+    Kd, Nd = wl.gemm("down")
+    for ly in layers:
+        run_layer(wl, ly)
+    torch.cuda.synchronize()
+    touched = [int(ly.route.result.num_groups.cpu()[0]) for ly in layers]
+    step_bytes = sum(route_bytes(wl.T, wl.E, wl.top_k) +
+                     gemm_bytes(n, wl.M, Ng, Kg) + gemm_bytes(n, wl.M, Nd, Kd) for n in touched)
+    dom_bytes = [gemm_bytes(n, wl.M, Ng, Kg) for n in touched]
+
+    # one step = every layer's launches, captured once as a HIP graph and
+    # replayed (the decode kernels are a few microseconds each: host launch
+    # overhead would otherwise dominate)
+    step = capture(lambda: [run_layer(wl, ly) for ly in layers]) if args.graph else None
+
+    def run_step():
+        if step is not None:
+            step.replay()
+        else:
+            for ly in layers:
+                run_layer(wl, ly)
+
+    for _ in range(args.warmup):
+        run_step()
+    # timed region: exactly `steps` steps, synchronised on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # dominant kernel: the gate_up GEMM of every layer launched back to back
+    # (one graph), HIP events on the same stream around each replay
+    def gate_up_only():
+        for ly in layers:
+            gate_up(wl, ly)
+    dom = capture(gate_up_only) if args.graph else None
+    reps = max(args.steps, 10)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        evs[i][0].record()
+        if dom is not None:
+            dom.replay()
+        else:
+            gate_up_only()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    dur_us = [s.elapsed_time(e) * 1e3 / L for s, e in evs]
+    avg_us = float(np.median(dur_us))
+    achieved = float(np.mean(dom_bytes)) / (avg_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: E={wl.E} top_k={wl.top_k} T={wl.T} M={wl.M}, gate_up "
+                        f"K={Kg} N={Ng} + down K={Kd} N={Nd}, {L} layers of distinct weights "
+                        f"per step (route/sort + gate_up with fused gather + down)",
+            "weights": "NF4 (block 64, fp32 absmax)", "activations": "bf16",
+            "global_batch": wl.T, "layers": L, "parallelism": "none (1 GPU)",
+            "launch": "HIP graph per step" if args.graph else "host launches",
+            "step_bytes": step_bytes, "touched_experts_per_layer": touched,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode-path grouped GEMM (gate_up), launched back to back over the layers",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_us, 3),
+            "algorithmic_bytes_per_launch": int(np.mean(dom_bytes)),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+    if args.cells:
+        time_cells(args.cells, dev)
+
+
+if __name__ == "__main__":
+    main()

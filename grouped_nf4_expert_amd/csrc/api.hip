@@ -136,23 +136,31 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
                                int64_t E, int64_t N, int64_t K, const int32_t* sizes,
                                const int32_t* ids, int64_t G, int64_t M, uint16_t* y,
                                void* ws, size_t ws_bytes, int32_t path, int32_t split_k,
-                               void* stream) {
+                               void* stream, const int32_t* slots = nullptr, int32_t slot_div = 1,
+                               int64_t T = 0) {
   if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
     return GNF4_ERR_INVALID_ARG;
   if (path < 0 || path > 2 || split_k < 0 || split_k > 16) return GNF4_ERR_INVALID_ARG;
+  if (slots && (slot_div < 1 || T < 0)) return GNF4_ERR_INVALID_ARG;
   if (M == 0 || G == 0) return GNF4_OK;
   if (N * (K / 2) >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) ||
       M * N >= ((int64_t)1 << 31) || E >= INT_MAX || G >= 65536)
     return GNF4_ERR_UNSUPPORTED;
+  if (slots && (T * slot_div >= ((int64_t)1 << 31) || T * K >= ((int64_t)1 << 31)))
+    return GNF4_ERR_UNSUPPORTED;
   if (!x || !packed || !absmax || !sizes || !ids || !y) return GNF4_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(sizes, 4) ||
-      !aligned(ids, 4) || !aligned(y, 2))
+      !aligned(ids, 4) || !aligned(y, 2) || (slots && !aligned(slots, 4)))
     return GNF4_ERR_INVALID_ARG;
   const void* ptrs[] = {x, packed, absmax, sizes, ids, y};
   for (const void* p : ptrs)
     if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  if (slots && !is_device_ptr(slots)) return GNF4_ERR_NOT_DEVICE_PTR;
 
   GemmArgs a;
+  a.slots = slots;
+  a.slot_div = slot_div;
+  a.T = (int)T;
   a.x = x;
   a.packed = packed;
   a.absmax = absmax;
@@ -218,6 +226,17 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
   const hipError_t e = launch_gather(x, sorted_slots, top_k, (int)T, (int)M, (int)K, x_sorted,
                                      (hipStream_t)stream);
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
+                                     int32_t top_k, const uint8_t* packed, const float* absmax,
+                                     int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                     const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                     uint16_t* y, void* workspace, size_t workspace_bytes,
+                                     int32_t path, int32_t split_k, void* stream) {
+  if (!sorted_slots) return GNF4_ERR_INVALID_ARG;
+  return gemm_common(x, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
+                     workspace, workspace_bytes, path, split_k, stream, sorted_slots, top_k, T);
 }
 
 size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,

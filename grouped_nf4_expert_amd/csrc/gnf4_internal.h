@@ -53,6 +53,46 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// ---- wavefront reductions on the DPP network (no LDS round trips).
+// Every lane of the wave must be active.  DPP controls (gfx9): quad_perm
+// [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_mirror = 0x140, row_half_mirror =
+// 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143, row_shr:n = 0x110 + n.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0xB1, 0xF>(0u, x));
+  x = max(x, dpp_u32<0x4E, 0xF>(0u, x));
+  x = max(x, dpp_u32<0x141, 0xF>(0u, x));
+  x = max(x, dpp_u32<0x140, 0xF>(0u, x));
+  x = max(x, dpp_u32<0x142, 0xA>(0u, x));
+  x = max(x, dpp_u32<0x143, 0xC>(0u, x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<0xB1, 0xF>(~0u, x));
+  x = min(x, dpp_u32<0x4E, 0xF>(~0u, x));
+  x = min(x, dpp_u32<0x141, 0xF>(~0u, x));
+  x = min(x, dpp_u32<0x140, 0xF>(~0u, x));
+  x = min(x, dpp_u32<0x142, 0xA>(~0u, x));
+  x = min(x, dpp_u32<0x143, 0xC>(~0u, x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Inclusive prefix sum across the wave (lane i gets sum of lanes 0..i).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += (int)dpp_u32<0x111, 0xF>(0u, (uint32_t)x);
+  x += (int)dpp_u32<0x112, 0xF>(0u, (uint32_t)x);
+  x += (int)dpp_u32<0x114, 0xF>(0u, (uint32_t)x);
+  x += (int)dpp_u32<0x118, 0xF>(0u, (uint32_t)x);
+  x += (int)dpp_u32<0x142, 0xA>(0u, (uint32_t)x);
+  x += (int)dpp_u32<0x143, 0xC>(0u, (uint32_t)x);
+  return x;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the C-ABI layer before these are called.
@@ -81,6 +121,11 @@ struct GemmArgs {
   const int32_t* ids;
   uint16_t* y;
   float* partial;     // split-K partials [S, M, N] (decode path)
+  // Optional fused gather: when `slots` is set, output row r uses activation
+  // row slots[r] / slot_div of x (x is then [T, K]); a slot outside
+  // [0, T * slot_div) leaves row r unwritten.
+  const int32_t* slots;
+  int slot_div, T;
   int E, N, K, G, M;
   int rows_max_decode;  // groups with size <= this take the decode path
   int rows_min_tile;    // groups with size >= this take the tile path
@@ -89,6 +134,7 @@ struct GemmArgs {
 struct DecodePlan {
   int L;        // lanes per weight row (8, 16, 32, 64)
   int NU;       // weight rows per lane
+  int R;        // activation rows per pass over a weight tile
   int S;        // K splits
   int cps;      // 32-code chunks per split
   int n_tiles;  // weight-row tiles per group

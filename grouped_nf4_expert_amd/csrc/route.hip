@@ -48,50 +48,51 @@ struct RouteArgs {
   int n_chunks;
 };
 
-// Top-k of one token by one wavefront.  Lane i ends up holding the i-th pick.
+// Order-preserving unsigned key of a float; -0.0 is folded onto +0.0 so the
+// two compare equal (and the lower id wins), as float comparison does.
+__device__ __forceinline__ uint32_t float_key(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Top-k of one token by one wavefront.  Lane i ends up holding the i-th
+// pick.  Each round is two DPP reductions: the largest key, then the lowest
+// expert id among the lanes holding it.
 __device__ void topk_token(const float* __restrict__ row, int E, int k, int lane,
                            int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                            int32_t* lds_ids) {
-  float v[kEPL];
+  uint32_t key[kEPL];
   uint32_t avail = 0;
 #pragma unroll
   for (int j = 0; j < kEPL; ++j) {
     const int e = lane + kWave * j;
-    v[j] = 0.0f;
+    key[j] = 0u;  // below every finite value's key
     if (e < E) {
-      v[j] = row[e];
+      key[j] = float_key(row[e]);
       avail |= 1u << j;
     }
   }
   float my_v = 0.0f;
   int my_id = 0;
   for (int i = 0; i < k; ++i) {
-    float bv = -INFINITY;
-    int bid = INT_MAX;
-    bool have = false;
+    uint32_t bk = 0u, bid = 0xffffffffu;
 #pragma unroll
     for (int j = 0; j < kEPL; ++j) {
-      if (avail & (1u << j)) {
-        if (!have || v[j] > bv) {  // strict: the lower id wins a tie
-          bv = v[j];
-          bid = lane + kWave * j;
-          have = true;
-        }
+      if ((avail & (1u << j)) && (bid == 0xffffffffu || key[j] > bk)) {
+        bk = key[j];
+        bid = (uint32_t)(lane + kWave * j);
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oid = __shfl_xor(bid, off, kWave);
-      if (ov > bv || (ov == bv && oid < bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if (lane == (bid & (kWave - 1))) avail &= ~(1u << (bid >> 6));
+    const uint32_t wk = wave_max_u32(bk);
+    const uint32_t wid = wave_min_u32(bk == wk ? bid : 0xffffffffu);
+    if (lane == (int)(wid & (kWave - 1))) avail &= ~(1u << (wid >> 6));
     if (lane == i) {
-      my_v = bv;
-      my_id = bid;
+      my_v = key_float(wk);
+      my_id = (int)wid;
     }
   }
   const float vmax = __shfl(my_v, 0, kWave);
@@ -104,16 +105,6 @@ __device__ void topk_token(const float* __restrict__ row, int E, int k, int lane
   }
 }
 
-// Inclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
-
 // Wave 0: exclusive scan of cnt[0..E) into base[] (LDS) and offsets[] (global),
 // compaction of the non-empty experts into the group arrays.
 __device__ void scan_and_groups(const int32_t* cnt, int32_t* base, const RouteArgs& a, int lane) {
@@ -121,10 +112,10 @@ __device__ void scan_and_groups(const int32_t* cnt, int32_t* base, const RouteAr
   for (int b0 = 0; b0 < a.E; b0 += kWave) {
     const int e = b0 + lane;
     const int c = (e < a.E) ? cnt[e] : 0;
-    const int inc = wave_inclusive_scan(c, lane);
+    const int inc = wave_incl_scan(c);
     const int excl = carry + inc - c;
     const int f = (c > 0) ? 1 : 0;
-    const int finc = wave_inclusive_scan(f, lane);
+    const int finc = wave_incl_scan(f);
     const int pos = gcarry + finc - f;
     if (e < a.E) {
       if (base) base[e] = excl;
@@ -167,15 +158,13 @@ __device__ void scatter_slots(const int32_t* ids, int s0, int s1, int32_t* base,
     const int rank = __popcll(peers & lt);
     int start = 0;
     if (active) start = base[e];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();  // every lane reads base[e] before any update
     if (active) {
       sorted[start + rank] = s;
       const bool leader = (peers & lt) == 0;
       if (leader) base[e] = start + __popcll(peers);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();  // LDS ops of one wave complete in order
   }
 }
 
@@ -195,7 +184,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a)
   __syncthreads();
   if (wave == 0) {
     scan_and_groups(s_cnt, s_base, a, lane);
-    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     scatter_slots(s_ids, 0, M, s_base, a.E, a.sorted, lane);
   }
@@ -254,7 +242,6 @@ __global__ __launch_bounds__(kWave) void route_scatter_kernel(RouteArgs a) {
   const int s0 = c * kChunkTokens * a.K;
   const int s1 = min(s0 + kChunkTokens * a.K, a.T * a.K);
   for (int s = s0 + lane; s < s1; s += kWave) s_ids[s - s0] = a.topk_ids[s];
-  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
   scatter_slots(s_ids, s0, s1, s_base, a.E, a.sorted, lane);
 }

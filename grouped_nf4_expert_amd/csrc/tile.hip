@@ -204,16 +204,31 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
 
     // x staging: thread owns 16-byte chunks q = tid + 256 * j of the pass
     // tile (row q / 16, K slice 8 * (q % 16))
+    // source activation row of each staged chunk (fused gather: via the
+    // slot table; -1 = row not present, staged as zeros)
+    int xsrc[kXChunks];
+#pragma unroll
+    for (int j = 0; j < kXChunks; ++j) {
+      const int row = (tid + kThreads * j) >> 4;
+      int src = -1;
+      if (row < rows) {
+        src = p0 + row;
+        if (a.g.slots) {
+          const int slot = a.g.slots[p0 + row];
+          src = (slot >= 0 && slot < a.g.T * a.g.slot_div) ? slot / a.g.slot_div : -1;
+        }
+      }
+      xsrc[j] = src;
+    }
     uint4 xr[kXChunks];
     auto load_x = [&](int step) {
       const int k0 = step * kStepK;
 #pragma unroll
       for (int j = 0; j < kXChunks; ++j) {
-        const int q = tid + kThreads * j;
-        const int row = q >> 4, c16 = q & 15;
+        const int c16 = (tid + kThreads * j) & 15;
         xr[j] = make_uint4(0, 0, 0, 0);
-        if (row < rows && k0 + 8 * c16 < K)
-          xr[j] = *reinterpret_cast<const uint4*>(a.g.x + (size_t)(p0 + row) * K + k0 + 8 * c16);
+        if (xsrc[j] >= 0 && k0 + 8 * c16 < K)
+          xr[j] = *reinterpret_cast<const uint4*>(a.g.x + (size_t)xsrc[j] * K + k0 + 8 * c16);
       }
     };
     auto store_x = [&](int buf) {
@@ -291,7 +306,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = p0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (row < r_end) a.g.y[(size_t)row * N + n] = f32_to_bf16(ldexpf(acc[rt][t][v], sexp[t]));
+          if (row >= r_end) continue;
+          if (a.g.slots) {
+            const int slot = a.g.slots[row];
+            if (slot < 0 || slot >= a.g.T * a.g.slot_div) continue;
+          }
+          a.g.y[(size_t)row * N + n] = f32_to_bf16(ldexpf(acc[rt][t][v], sexp[t]));
         }
       }
     }

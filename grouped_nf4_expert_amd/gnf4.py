@@ -67,6 +67,9 @@ def library():
     lib.gnf4_grouped_gemm_workspace_size_ex.argtypes = [i64, i64, i64, i64, i64, i32, i32]
     lib.gnf4_grouped_gemm.restype = ctypes.c_int
     lib.gnf4_grouped_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz, vp]
+    lib.gnf4_grouped_gemm_gather.restype = ctypes.c_int
+    lib.gnf4_grouped_gemm_gather.argtypes = [vp, i64, vp, i32, vp, vp, i64, i64, i64, vp, vp, i64,
+                                             i64, vp, vp, sz, i32, i32, vp]
     lib.gnf4_grouped_gemm_ex.restype = ctypes.c_int
     lib.gnf4_grouped_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp,
                                          sz, i32, i32, vp]
@@ -194,9 +197,12 @@ def gemm_workspace_size(M, N, K, G, E, path=PATH_AUTO, split_k=0):
 
 
 def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None, y=None,
-                 workspace=None, path=PATH_AUTO, split_k=0):
+                 workspace=None, path=PATH_AUTO, split_k=0, sorted_slots=None, top_k=1):
     """y[M, N] (bf16) = per-group x_sorted[rows] @ dequant(W[expert])^T.
 
+    With ``sorted_slots`` given, ``x_sorted`` holds the token rows [T, K] and
+    output row r uses token sorted_slots[r] // top_k (the gather is fused
+    into the GEMM); M is then ``sorted_slots.numel()``.
     ``G`` defaults to ``min(len(group_sizes), M)``, which is exact for the
     compact groups route_sort emits (non-empty groups come first).
     """
@@ -205,7 +211,12 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
     _need(absmax, "absmax", torch.float32, 3)
     _need(group_sizes, "group_sizes", torch.int32, 1)
     _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
-    M, K = x_sorted.shape
+    rows, K = x_sorted.shape
+    if sorted_slots is not None:
+        _need(sorted_slots, "sorted_slots", torch.int32, 1)
+        M = sorted_slots.numel()
+    else:
+        M = rows
     E, N, half_k = packed.shape
     if half_k * 2 != K or absmax.shape != (E, N, K // 64):
         raise ValueError("packed/absmax shapes do not match x_sorted's K")
@@ -219,8 +230,14 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x_sorted.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().gnf4_grouped_gemm_ex(
-        _ptr(x_sorted), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes),
-        _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes, path, split_k,
-        _stream()), "gnf4_grouped_gemm")
+    if sorted_slots is None:
+        _check(library().gnf4_grouped_gemm_ex(
+            _ptr(x_sorted), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes),
+            _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes, path, split_k,
+            _stream()), "gnf4_grouped_gemm")
+    else:
+        _check(library().gnf4_grouped_gemm_gather(
+            _ptr(x_sorted), rows, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(absmax), E, N, K,
+            _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
+            path, split_k, _stream()), "gnf4_grouped_gemm_gather")
     return y

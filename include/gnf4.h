@@ -210,6 +210,31 @@ gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed
                                  void* workspace, size_t workspace_bytes,
                                  int32_t path, int32_t split_k, void* stream);
 
+/*
+ * gnf4_grouped_gemm_gather -- gnf4_gather_rows fused into the grouped GEMM:
+ * output row r is x[sorted_slots[r] / top_k, :] . dequant(W[expert])^T, so
+ * the grouped activations are never written out.
+ *
+ * Page "grouped-nf4-gemm -- single-launch W4A16 GEMM ...", opening section
+ * (grouped rows "after the usual token->expert sort"); landing page
+ * "grouped-nf4-gemm", "Use this when" (fold the decode step's small launches).
+ *
+ *   x             [T, K] bf16 bits: token activations (not grouped), 16-byte aligned
+ *   sorted_slots  [M] int32 as gnf4_route_sort writes them; top_k >= 1
+ *   other arguments as in gnf4_grouped_gemm_ex.
+ *
+ * Same arithmetic and tolerance as gnf4_grouped_gemm applied to the gathered
+ * rows; a row whose slot lies outside [0, T * top_k) is not written.
+ * Errors: as gnf4_grouped_gemm_ex, plus GNF4_ERR_INVALID_ARG for a null
+ * sorted_slots or top_k < 1.
+ */
+gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
+                                     int32_t top_k, const uint8_t* packed, const float* absmax,
+                                     int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                     const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                     uint16_t* y, void* workspace, size_t workspace_bytes,
+                                     int32_t path, int32_t split_k, void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

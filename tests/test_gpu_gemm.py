@@ -96,15 +96,15 @@ def _custom(E, N, K, sizes, ids, M, seed=0, w_scale=None, x=None):
 
 def _run_custom(c, path, split_k=0, canary=True):
     M, N = c["M"], c["N"]
-    full = torch.full((M + 2, N), -777.0, dtype=torch.bfloat16, device=DEV)
+    full = torch.full((M + 2, N), -512.0, dtype=torch.bfloat16, device=DEV)
     y = full[1:M + 1]
     gnf4.grouped_gemm(c["xs"], c["packed"], c["absmax"], c["sizes"], c["ids"],
                       G=c["sizes"].numel(), y=y, path=path, split_k=split_k)
     torch.cuda.synchronize()
     f = full.float().cpu().numpy()
     if canary:
-        assert np.all(f[0] == -777.0) and np.all(f[M + 1] == -777.0), "guard rows written"
-        assert np.all(f[1:M + 1][~c["written"]] == -777.0), "uncovered rows written"
+        assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0), "guard rows written"
+        assert np.all(f[1:M + 1][~c["written"]] == -512.0), "uncovered rows written"
     return y
 
 
@@ -232,3 +232,45 @@ def test_rejects_host_tensors():
     s = torch.tensor([4], dtype=torch.int32, device=DEV)
     with pytest.raises(gnf4.Gnf4Error, match="oracle"):
         gnf4.grouped_gemm(x, packed, absmax, s, s.clone())
+
+
+@pytest.mark.parametrize("name", ["tiny", "olmoe", "qwen3_t8", "gptoss_t256"])
+@pytest.mark.parametrize("path", [AUTO, DEC, TILE])
+def test_fused_gather(name, path):
+    """gnf4_grouped_gemm_gather on token rows == oracle on the gathered rows."""
+    wl = wls.WORKLOADS[name]
+    gemm = "w" if name == "tiny" else "gate_up"
+    c = _workload_case(name, gemm)
+    x_tok = wls.token_activations(wl, c["K"])
+    note(f"gemm fused gather {name} path={path}")
+    y = gnf4.grouped_gemm(bf16_dev(x_tok), c["packed"], c["absmax"], c["r"].group_sizes,
+                          c["r"].group_expert_ids, path=path, sorted_slots=c["r"].sorted_slots,
+                          top_k=wl.top_k)
+    torch.cuda.synchronize()
+    check_gemm(y, c["y_ref"], c["written"], f"fused gather {name} path {path}")
+
+
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_fused_gather_bad_slots_skip_rows(path):
+    E, N, K, T, top_k = 3, 64, 256, 10, 2
+    sizes, ids = [4, 12, 4], [2, 0, 1]
+    M = sum(sizes)
+    rng = np.random.default_rng(31)
+    slots = rng.integers(0, T * top_k, M).astype(np.int32)
+    slots[[1, 7, 18]] = [-1, T * top_k, 10 ** 6]
+    x_tok = wls.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    x_rows = np.zeros((M, K), np.float32)
+    ok = (slots >= 0) & (slots < T * top_k)
+    x_rows[ok] = x_tok[slots[ok] // top_k]
+    c = _custom(E, N, K, sizes, ids, M, seed=32, x=x_rows)
+    written = c["written"] & ok
+    full = torch.full((M + 2, N), -512.0, dtype=torch.bfloat16, device=DEV)
+    note(f"gemm fused gather bad slots path={path}")
+    gnf4.grouped_gemm(bf16_dev(x_tok), c["packed"], c["absmax"], c["sizes"], c["ids"], G=3,
+                      y=full[1:M + 1], path=path,
+                      sorted_slots=torch.from_numpy(slots).to(DEV), top_k=top_k)
+    torch.cuda.synchronize()
+    f = full.float().cpu().numpy()
+    assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0)
+    assert np.all(f[1:M + 1][~written] == -512.0), "rows with bad slots were written"
+    check_gemm(full[1:M + 1], c["y_ref"], written, f"bad slots path {path}")
