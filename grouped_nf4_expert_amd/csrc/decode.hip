@@ -21,16 +21,18 @@
 //  * R activation rows (a compile-time choice from the host-known rows per
 //    group) are converted to fp32 once per chunk so one decoded code feeds R
 //    multiply-adds; larger groups loop over chunks of R rows;
-//  * a code's level is read from a 16-entry fp32 table in LDS at a 16-byte
-//    stride (level q at bank 4q: conflict-free for any mix of codes, and the
-//    byte offset is a single mask of a packed byte), multiplied and
-//    accumulated in fp32; the block absmax is applied once per 32 codes;
+//  * a code's level is read from a 16-entry fp32 table in LDS at an 8-byte
+//    stride (level q at bank 2q: conflict-free for any mix of codes whether
+//    the LDS has 32 or 64 banks, and the byte offset is one masked byte of a
+//    shifted packed dword), multiplied and accumulated in fp32; the block
+//    absmax is applied once per 32 codes;
 //  * team partial sums are combined with a fixed butterfly and either
 //    rounded to bf16 or, when K is split across workgroups to fill the
 //    machine, written as fp32 partials that a second kernel sums in split
 //    order (deterministic).
 
 #include <limits.h>
+#include <stdlib.h>
 
 #include "gnf4_internal.h"
 
@@ -136,7 +138,9 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int K, const int (&xro
 // arithmetic waits only for its own weight bytes.
 template <int L, int NU, int R, bool MULTI>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
-  __shared__ float s_lut[kWaves * 64];  // per wavefront: 16 levels at a 16-byte stride
+  // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
+  // offset is the whole address (no per-read base add)
+  __shared__ float s_lut[32];
   const int g = blockIdx.y;
   const int sz = a.g.sizes[g];
   const int e = a.g.ids[g];
@@ -156,15 +160,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   const int c_end = min(c_begin + a.cps, a.cpr);
   const int c_first = c_begin + tl;
 
-  // (1) metadata; each wavefront keeps its own copy of the table (no barrier)
+  // (1) metadata
   int part = 0;
   for (int i = lane; i < g; i += kWave) part += max(a.g.sizes[i], 0);
   const bool gather = a.g.slots != nullptr;
   const bool slots_in_lanes = gather && a.g.M <= kWave;
   int my_slot = 0;
   if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
-  float* lut = s_lut + wave * 64;
-  if (lane < 16) lut[4 * lane] = nf4_level(lane);
+  // every wavefront writes the same values before its own reads; LDS
+  // operations of one wavefront complete in order, so no barrier is needed
+  const float* lut = s_lut;
+  if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const int r_begin = __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
   const int r_end = min(r_begin + sz, a.g.M);
   __builtin_amdgcn_wave_barrier();
@@ -219,18 +225,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
         const uint32_t d[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          // LUT byte offsets 16 * code: the high code of byte b is byte b & 0xf0;
-          // after a 4-bit left shift the low code sits there instead.
-          const uint32_t dsh = d[w] << 4;
+          // LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
+          // byte b hold its high code; after a left shift by 3, its low code.
+          const uint32_t dh = d[w] >> 1;
+          const uint32_t dl = d[w] << 3;
           uint32_t oh[4], ol[4];
-          oh[0] = byte_and<0>(d[w], 0xf0u);
-          oh[1] = byte_and<1>(d[w], 0xf0u);
-          oh[2] = byte_and<2>(d[w], 0xf0u);
-          oh[3] = byte_and<3>(d[w], 0xf0u);
-          ol[0] = byte_and<0>(dsh, 0xf0u);
-          ol[1] = byte_and<1>(dsh, 0xf0u);
-          ol[2] = byte_and<2>(dsh, 0xf0u);
-          ol[3] = byte_and<3>(dsh, 0xf0u);
+          oh[0] = byte_and<0>(dh, 0x78u);
+          oh[1] = byte_and<1>(dh, 0x78u);
+          oh[2] = byte_and<2>(dh, 0x78u);
+          oh[3] = byte_and<3>(dh, 0x78u);
+          ol[0] = byte_and<0>(dl, 0x78u);
+          ol[1] = byte_and<1>(dl, 0x78u);
+          ol[2] = byte_and<2>(dl, 0x78u);
+          ol[3] = byte_and<3>(dl, 0x78u);
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const float vh = lut_at(lut, oh[b]);
@@ -346,6 +353,9 @@ hipError_t launch_LN(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stre
 template <int L>
 hipError_t launch_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   switch (p.NU) {
+#ifdef GNF4_TUNING
+    case 8: return launch_LN<L, 8>(a, p, stream);
+#endif
     case 4: return launch_LN<L, 4>(a, p, stream);
     case 2: return launch_LN<L, 2>(a, p, stream);
     default: return launch_LN<L, 1>(a, p, stream);
@@ -354,7 +364,8 @@ hipError_t launch_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t strea
 
 }  // namespace
 
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, int num_cus) {
+static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, int split_k,
+                                   int num_cus) {
   const int cpr = (int)(K / 32);
   const int64_t g_eff = G < M ? G : M;
   const int64_t target = 2LL * num_cus;  // workgroups that keep every CU busy
@@ -397,6 +408,18 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, 
     if (split_k > 0) break;
   }
   return best;
+}
+
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, int num_cus) {
+  DecodePlan p = plan_decode_rule(M, N, K, G, split_k, num_cus);
+#ifdef GNF4_TUNING  // experiment builds only: override the launch rule
+  if (const char* v = getenv("GNF4_TUNE_NU")) {
+    p.NU = atoi(v);
+    p.rows_per_block = kWaves * (kWave / p.L) * p.NU;
+    p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
+  }
+#endif
+  return p;
 }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N) {

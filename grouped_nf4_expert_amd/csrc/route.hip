@@ -7,20 +7,25 @@
 //
 // Design (all integer work bit-exact and free of atomics that decide an
 // order):
-//  * top-k: one wavefront per token.  Each lane holds up to 16 logits
-//    (experts lane, lane+64, ...); k rounds of a wave-wide arg-max over
-//    (logit desc, id asc) pick the experts.  Weights are the softmax of the k
-//    selected logits in fp32.
-//  * sort: a counting sort by expert over chunks of tokens.  Per chunk an LDS
-//    histogram (counts commute, so LDS atomics are safe); an exclusive scan
-//    over (expert, chunk) gives every chunk's first row per expert; one
-//    wavefront per chunk then walks its slots in ascending order, ranking
-//    equal experts inside each 64-slot batch with ballots, so the output is
-//    the stable order.
-//  * small batches (every decode step) fit one chunk and run as ONE launch;
-//    larger ones use three (top-k + histogram, scan, scatter).
+//  * top-k by rank: each logit becomes a unique 64-bit key (order-preserving
+//    float key in the high half, the complement of the expert id in the low
+//    half: larger = better, equal logits go to the lower id).  One
+//    wavefront per token; a lane ranks each of its keys against every key of
+//    the token (broadcast with readlane) -- independent compare-adds instead
+//    of k dependent arg-max rounds -- and the keys ranked below k are the
+//    picks, in order.  Weights are the softmax of the k picks in fp32.
+//  * a single token (every batch-1 decode step) needs no sort at all: its
+//    picks are distinct experts, so each pick's place in expert order is a
+//    ballot prefix count; one wavefront writes every output.
+//  * more tokens: a counting sort by expert over chunks of 64 tokens.  Per
+//    chunk an LDS histogram (counts commute, so LDS atomics are safe); an
+//    exclusive scan over (expert, chunk) gives every chunk's first row per
+//    expert; one wavefront per chunk then walks its slots in ascending order,
+//    ranking equal experts inside each 64-slot batch with ballots, so the
+//    output is the stable order.  One chunk runs as ONE launch (16
+//    wavefronts); larger batches use three (top-k + histogram, scan,
+//    scatter).
 
-#include <limits.h>
 #include <math.h>
 
 #include "gnf4_internal.h"
@@ -28,11 +33,11 @@
 namespace gnf4 {
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;  // 16 wavefronts: one token each at a time
+constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kChunkTokens = 64;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-constexpr int kEPL = kMaxE / kWave;  // logits held per lane
 
 struct RouteArgs {
   const float* logits;
@@ -55,53 +60,132 @@ __device__ __forceinline__ uint32_t float_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Top-k of one token by one wavefront.  Lane i ends up holding the i-th
-// pick.  Each round is two DPP reductions: the largest key, then the lowest
-// expert id among the lanes holding it.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __int_as_float((int)dpp_u32<0xB1, 0xF>(0u, __float_as_uint(v)));
+  v += __int_as_float((int)dpp_u32<0x4E, 0xF>(0u, __float_as_uint(v)));
+  v += __int_as_float((int)dpp_u32<0x141, 0xF>(0u, __float_as_uint(v)));
+  v += __int_as_float((int)dpp_u32<0x140, 0xF>(0u, __float_as_uint(v)));
+  v += __int_as_float((int)dpp_u32<0x142, 0xA>(0u, __float_as_uint(v)));
+  v += __int_as_float((int)dpp_u32<0x143, 0xC>(0u, __float_as_uint(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Ranks of one token's E logits.  Entry s of a lane is expert lane + 64 s;
+// rank = number of better entries.  Returns the logits in `val`.
+template <int EPL>
+__device__ __forceinline__ void rank_token(const float* __restrict__ row, int E, int lane,
+                                           float (&val)[EPL], int (&rank)[EPL]) {
+  uint64_t key[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const int e = lane + kWave * s;
+    val[s] = (e < E) ? row[e] : 0.0f;
+    key[s] = (e < E) ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
+                     : 0ull;
+    rank[s] = 0;
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < EPL; ++s2) {
+    if (kWave * s2 >= E) break;
+    for (int j = 0; j < kWave; ++j) {
+      const uint64_t kj = readlane64(key[s2], j);
+#pragma unroll
+      for (int s = 0; s < EPL; ++s) rank[s] += (kj > key[s]) ? 1 : 0;
+    }
+  }
+}
+
+// Top-k of one token: ids/weights to global memory (and ids to LDS).
+template <int EPL>
 __device__ void topk_token(const float* __restrict__ row, int E, int k, int lane,
                            int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                            int32_t* lds_ids) {
-  uint32_t key[kEPL];
-  uint32_t avail = 0;
+  float val[EPL];
+  int rank[EPL];
+  rank_token<EPL>(row, E, lane, val, rank);
+  // the best logit (rank 0) for a stable softmax
+  float vbest = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kEPL; ++j) {
-    const int e = lane + kWave * j;
-    key[j] = 0u;  // below every finite value's key
-    if (e < E) {
-      key[j] = float_key(row[e]);
-      avail |= 1u << j;
+  for (int s = 0; s < EPL; ++s) {
+    // exactly one entry of the token has rank 0
+    const uint64_t has = __ballot(rank[s] == 0);
+    if (has) {
+      const int src = __ffsll((unsigned long long)has) - 1;
+      vbest = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[s]), src));
     }
   }
-  float my_v = 0.0f;
-  int my_id = 0;
-  for (int i = 0; i < k; ++i) {
-    uint32_t bk = 0u, bid = 0xffffffffu;
+  float ex[EPL];
+  float part = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kEPL; ++j) {
-      if ((avail & (1u << j)) && (bid == 0xffffffffu || key[j] > bk)) {
-        bk = key[j];
-        bid = (uint32_t)(lane + kWave * j);
-      }
-    }
-    const uint32_t wk = wave_max_u32(bk);
-    const uint32_t wid = wave_min_u32(bk == wk ? bid : 0xffffffffu);
-    if (lane == (int)(wid & (kWave - 1))) avail &= ~(1u << (wid >> 6));
-    if (lane == i) {
-      my_v = key_float(wk);
-      my_id = (int)wid;
+  for (int s = 0; s < EPL; ++s) {
+    ex[s] = (rank[s] < k) ? expf(val[s] - vbest) : 0.0f;
+    part += ex[s];
+  }
+  const float sum = wave_sum_f32(part);
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    if (rank[s] < k) {
+      const int e = lane + kWave * s;
+      ids_out[rank[s]] = e;
+      w_out[rank[s]] = ex[s] / sum;
+      if (lds_ids) lds_ids[rank[s]] = e;
     }
   }
-  const float vmax = __shfl(my_v, 0, kWave);
-  const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = ex / sum;
-    if (lds_ids) lds_ids[lane] = my_id;
+}
+
+// A single token: top-k and the whole sort in one wavefront.
+template <int EPL>
+__global__ __launch_bounds__(kWave) void route_one_token_kernel(RouteArgs a) {
+  const int lane = threadIdx.x;
+  float val[EPL];
+  int rank[EPL];
+  rank_token<EPL>(a.logits, a.E, lane, val, rank);
+  float vbest = 0.0f;
+  uint64_t sel[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const uint64_t has = __ballot(rank[s] == 0);
+    if (has) vbest = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[s]),
+                                                              __ffsll((unsigned long long)has) - 1));
+    sel[s] = __ballot(rank[s] < a.K);
+  }
+  float ex[EPL];
+  float part = 0.0f;
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    ex[s] = (rank[s] < a.K) ? expf(val[s] - vbest) : 0.0f;
+    part += ex[s];
+  }
+  const float sum = wave_sum_f32(part);
+  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  int before = 0;  // picks with a lower expert id than entry (s, lane)
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const int e = lane + kWave * s;
+    const int pos = before + __popcll(sel[s] & lt);
+    if (e < a.E) a.offsets[e] = pos;
+    if (rank[s] < a.K) {
+      a.topk_ids[rank[s]] = e;
+      a.topk_w[rank[s]] = ex[s] / sum;
+      a.sorted[pos] = rank[s];  // slot t * k + j with t = 0
+      a.gsizes[pos] = 1;
+      a.gids[pos] = e;
+    }
+    before += __popcll(sel[s]);
+  }
+  if (lane == 0) {
+    a.offsets[a.E] = a.K;
+    a.ngroups[0] = a.K;
+  }
+  for (int i = a.K + lane; i < a.E; i += kWave) {
+    a.gsizes[i] = 0;
+    a.gids[i] = 0;
   }
 }
 
@@ -125,8 +209,8 @@ __device__ void scan_and_groups(const int32_t* cnt, int32_t* base, const RouteAr
         a.gids[pos] = e;
       }
     }
-    carry += __shfl(inc, kWave - 1, kWave);
-    gcarry += __shfl(finc, kWave - 1, kWave);
+    carry += __builtin_amdgcn_readlane(inc, kWave - 1);
+    gcarry += __builtin_amdgcn_readlane(finc, kWave - 1);
   }
   if (lane == 0) {
     a.offsets[a.E] = carry;
@@ -169,16 +253,17 @@ __device__ void scatter_slots(const int32_t* ids, int s0, int s1, int32_t* base,
 }
 
 // Whole sort in one workgroup: T * K fits one chunk.
+template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a) {
   __shared__ int32_t s_ids[kChunkTokens * kMaxK];
   __shared__ int32_t s_cnt[kMaxE];
   __shared__ int32_t s_base[kMaxE];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int M = a.T * a.K;
-  for (int t = wave; t < a.T; t += kRouteThreads / kWave)
-    topk_token(a.logits + (size_t)t * a.E, a.E, a.K, lane, a.topk_ids + (size_t)t * a.K,
-               a.topk_w + (size_t)t * a.K, s_ids + t * a.K);
   for (int e = threadIdx.x; e < a.E; e += kRouteThreads) s_cnt[e] = 0;
+  for (int t = wave; t < a.T; t += kRouteWaves)
+    topk_token<EPL>(a.logits + (size_t)t * a.E, a.E, a.K, lane, a.topk_ids + (size_t)t * a.K,
+                    a.topk_w + (size_t)t * a.K, s_ids + t * a.K);
   __syncthreads();
   for (int s = threadIdx.x; s < M; s += kRouteThreads) atomicAdd(&s_cnt[s_ids[s]], 1);
   __syncthreads();
@@ -190,6 +275,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a)
 }
 
 // Large batches, step 1: top-k of the chunk's tokens and its expert histogram.
+template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_hist_kernel(RouteArgs a) {
   __shared__ int32_t s_ids[kChunkTokens * kMaxK];
   __shared__ int32_t s_cnt[kMaxE];
@@ -197,10 +283,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_hist_kernel(RouteArg
   const int c = blockIdx.x;
   const int t0 = c * kChunkTokens;
   const int t1 = min(t0 + kChunkTokens, a.T);
-  for (int t = t0 + wave; t < t1; t += kRouteThreads / kWave)
-    topk_token(a.logits + (size_t)t * a.E, a.E, a.K, lane, a.topk_ids + (size_t)t * a.K,
-               a.topk_w + (size_t)t * a.K, s_ids + (t - t0) * a.K);
   for (int e = threadIdx.x; e < a.E; e += kRouteThreads) s_cnt[e] = 0;
+  for (int t = t0 + wave; t < t1; t += kRouteWaves)
+    topk_token<EPL>(a.logits + (size_t)t * a.E, a.E, a.K, lane, a.topk_ids + (size_t)t * a.K,
+                    a.topk_w + (size_t)t * a.K, s_ids + (t - t0) * a.K);
   __syncthreads();
   const int n = (t1 - t0) * a.K;
   for (int s = threadIdx.x; s < n; s += kRouteThreads) atomicAdd(&s_cnt[s_ids[s]], 1);
@@ -212,6 +298,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_hist_kernel(RouteArg
 // the groups, and every chunk's base row per expert (in place of its count).
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
   __shared__ int32_t s_tot[kMaxE];
+  __shared__ int32_t s_base[kMaxE];
   const int e = threadIdx.x;
   if (e < a.E) {
     int run = 0;
@@ -224,7 +311,6 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
     s_tot[e] = run;
   }
   __syncthreads();
-  __shared__ int32_t s_base[kMaxE];
   if (threadIdx.x < kWave) scan_and_groups(s_tot, s_base, a, threadIdx.x);
   __syncthreads();
   if (e < a.E) {
@@ -254,6 +340,20 @@ __global__ void route_empty_kernel(RouteArgs a) {
     a.gids[i] = 0;
   }
   if (threadIdx.x == 0) a.ngroups[0] = 0;
+}
+
+template <int EPL>
+void launch_epl(const RouteArgs& a, const RoutePlan& plan, hipStream_t stream) {
+  if (a.T == 1) {
+    hipLaunchKernelGGL(route_one_token_kernel<EPL>, dim3(1), dim3(kWave), 0, stream, a);
+  } else if (plan.n_chunks == 1) {
+    hipLaunchKernelGGL(route_fused_kernel<EPL>, dim3(1), dim3(kRouteThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(route_topk_hist_kernel<EPL>, dim3(plan.n_chunks), dim3(kRouteThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(plan.n_chunks), dim3(kWave), 0, stream, a);
+  }
 }
 
 }  // namespace
@@ -288,13 +388,16 @@ hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32
   a.n_chunks = plan.n_chunks;
   if (T == 0) {
     hipLaunchKernelGGL(route_empty_kernel, dim3(1), dim3(256), 0, stream, a);
-  } else if (plan.n_chunks == 1) {
-    hipLaunchKernelGGL(route_fused_kernel, dim3(1), dim3(kRouteThreads), 0, stream, a);
+  } else if (E <= 64) {
+    launch_epl<1>(a, plan, stream);
+  } else if (E <= 128) {
+    launch_epl<2>(a, plan, stream);
+  } else if (E <= 256) {
+    launch_epl<4>(a, plan, stream);
+  } else if (E <= 512) {
+    launch_epl<8>(a, plan, stream);
   } else {
-    hipLaunchKernelGGL(route_topk_hist_kernel, dim3(plan.n_chunks), dim3(kRouteThreads), 0,
-                       stream, a);
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(plan.n_chunks), dim3(kWave), 0, stream, a);
+    launch_epl<16>(a, plan, stream);
   }
   return hipGetLastError();
 }
