@@ -88,13 +88,6 @@ __device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
 }
 
-// Row offset of group g: sum of max(size, 0) over the groups before it.
-__device__ __forceinline__ int group_row_offset(const int32_t* sizes, int g, int lane) {
-  int part = 0;
-  for (int i = lane; i < g; i += kWave) part += max(sizes[i], 0);
-  return __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
-}
-
 template <int NU>
 __device__ __forceinline__ void load_weights(const uint8_t* wexp, const float* aexp,
                                              size_t row_bytes, int bpr, int N, int n_base, int c,
@@ -141,38 +134,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
   __shared__ float s_lut[32];
-  const int g = blockIdx.y;
-  const int sz = a.g.sizes[g];
-  const int e = a.g.ids[g];
-  if (sz <= 0 || sz > a.g.rows_max_decode || e < 0 || e >= a.g.E) return;
   constexpr int RPW = kWave / L;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const bool gather = a.g.slots != nullptr;
+  const bool slots_in_lanes = gather && a.g.M <= kWave;
+  // (1) metadata: the slot table (issued first, independent of the group)
+  // and the group this workgroup serves
+  int my_slot = 0;
+  if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
+  GroupRef gr;
+  if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y, gr))
+    return;
   const int tile = blockIdx.x % a.n_tiles;
   const int s = blockIdx.x / a.n_tiles;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int team = lane / L, tl = lane % L;
   const int N = a.g.N, K = a.g.K;
   const int n_base = tile * a.rows_per_block + wave * (RPW * NU) + team * NU;
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
-  const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
-  const float* aexp = a.g.absmax + (size_t)e * N * bpr;
+  const uint8_t* wexp = a.g.packed + (size_t)gr.expert * N * row_bytes;
+  const float* aexp = a.g.absmax + (size_t)gr.expert * N * bpr;
   const int c_begin = s * a.cps;
   const int c_end = min(c_begin + a.cps, a.cpr);
   const int c_first = c_begin + tl;
-
-  // (1) metadata
-  int part = 0;
-  for (int i = lane; i < g; i += kWave) part += max(a.g.sizes[i], 0);
-  const bool gather = a.g.slots != nullptr;
-  const bool slots_in_lanes = gather && a.g.M <= kWave;
-  int my_slot = 0;
-  if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
   // every wavefront writes the same values before its own reads; LDS
   // operations of one wavefront complete in order, so no barrier is needed
   const float* lut = s_lut;
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
-  const int r_begin = __builtin_amdgcn_readlane(wave_incl_scan(part), 63);
-  const int r_end = min(r_begin + sz, a.g.M);
+  const int r_begin = gr.row;
+  const int r_end = min(r_begin + gr.size, a.g.M);
   __builtin_amdgcn_wave_barrier();
 
   for (int r0 = r_begin; r0 < r_end; r0 += R) {
@@ -290,18 +280,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 
 // Sum the S split partials of every decode-path row in split order -> bf16.
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) {
-  __shared__ int s_off;
-  const int g = blockIdx.y;
-  const int sz = a.g.sizes[g];
-  const int e = a.g.ids[g];
-  if (sz <= 0 || sz > a.g.rows_max_decode || e < 0 || e >= a.g.E) return;
-  if (threadIdx.x < kWave) {
-    const int off = group_row_offset(a.g.sizes, g, threadIdx.x);
-    if (threadIdx.x == 0) s_off = off;
-  }
-  __syncthreads();
-  const int r_begin = s_off;
-  const int r_end = min(r_begin + sz, a.g.M);
+  GroupRef gr;
+  if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y, gr))
+    return;
+  const int r_begin = gr.row;
+  const int r_end = min(r_begin + gr.size, a.g.M);
   const int n = blockIdx.x * kThreads + threadIdx.x;
   if (n >= a.g.N) return;
   const size_t plane = (size_t)a.g.M * a.g.N;
@@ -336,7 +319,7 @@ int pick_lanes(int cps) {
 
 template <int L, int NU, bool MULTI>
 hipError_t launch_LNM(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.n_tiles * p.S), (unsigned)a.g.G);
+  const dim3 grid((unsigned)(p.n_tiles * p.S), (unsigned)group_slots(a.g.G, a.g.M, 1));
   switch (p.R) {
     case 4: hipLaunchKernelGGL((decode_kernel<L, NU, 4, MULTI>), grid, dim3(kThreads), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_kernel<L, NU, 2, MULTI>), grid, dim3(kThreads), 0, stream, a); break;
@@ -442,7 +425,7 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
     default: err = launch_L<8>(a, p, stream); break;
   }
   if (err != hipSuccess || p.S == 1) return err;
-  const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)g.G);
+  const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)group_slots(g.G, g.M, 1));
   hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

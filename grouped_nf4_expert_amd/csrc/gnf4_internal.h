@@ -93,6 +93,65 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// One group of a grouped GEMM, as located by find_group.
+struct GroupRef {
+  int g;       // index into sizes / ids
+  int size;    // rows
+  int expert;  // expert id
+  int row;     // first row: sum of max(size, 0) over the groups before g, capped at M
+};
+
+// The j-th group (in group order) whose size lies in [lo, hi] (lo >= 1) and
+// whose expert id lies in [0, E): kernels launch one slot per group they can
+// handle instead of one per entry of `sizes`, so empty groups cost no
+// workgroups.  Call with the whole wavefront active; every lane gets the same
+// result.  Sizes are clamped to [0, M] before summing (M < 2^25, so the
+// wavefront's partial sums fit an int) and the running row count saturates at
+// M, where nothing is written.  All loads of a 256-group chunk are issued
+// before any is used.
+__device__ __forceinline__ bool find_group(const int32_t* sizes, const int32_t* ids, int G,
+                                           int E, int M, int lo, int hi, int j, GroupRef& out) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  int seen = 0, rows = 0;
+  for (int c0 = 0; c0 < G; c0 += 4 * kWave) {
+    int sv[4], ev[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = c0 + q * kWave + lane;
+      sv[q] = i < G ? sizes[i] : 0;
+      ev[q] = i < G ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = sv[q] >= lo && sv[q] <= hi && ev[q] >= 0 && ev[q] < E;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      const int cnt = __builtin_popcountll(m);
+      const int incl = wave_incl_scan(min(max(sv[q], 0), M));
+      if (j < seen + cnt) {
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint64_t pick = __builtin_amdgcn_ballot_w64(ok && below == j - seen);
+        const int src = __builtin_ctzll(pick);
+        const int sz = __builtin_amdgcn_readlane(sv[q], src);
+        out.g = c0 + q * kWave + src;
+        out.size = sz;
+        out.expert = __builtin_amdgcn_readlane(ev[q], src);
+        out.row = min(rows + __builtin_amdgcn_readlane(incl, src) - min(sz, M), M);
+        return true;
+      }
+      seen += cnt;
+      rows = min(rows + __builtin_amdgcn_readlane(incl, 63), M);
+    }
+  }
+  return false;
+}
+
+// Upper bound on the groups with at least `lo` rows among G groups of M rows.
+inline int64_t group_slots(int64_t G, int64_t M, int64_t lo) {
+  const int64_t cap = M / (lo > 0 ? lo : 1);
+  return G < cap ? G : cap;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the C-ABI layer before these are called.

@@ -33,6 +33,8 @@
 //    reads are bank-conflict-free) and stored in the same K order the weight
 //    decode produces, so A and B fragments agree slot by slot.
 
+#include <limits.h>
+
 #include "gnf4_internal.h"
 
 namespace gnf4 {
@@ -52,7 +54,7 @@ constexpr int kXChunks = kPassRows * (kStepK / 8) / kThreads;  // 16-byte loads 
 struct TileKArgs {
   GemmArgs g;
   int n_tiles;
-  int n_work;   // G * n_tiles
+  int n_work;   // group slots * n_tiles
 };
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -129,37 +131,25 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
   return r;
 }
 
-__device__ __forceinline__ int group_row_offset(const int32_t* sizes, int g, int lane) {
-  int sum = 0;
-  for (int i = lane; i < g; i += kWave) sum += max(sizes[i], 0);
-  return wave_sum(sum);
-}
-
 __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
-  __shared__ int s_off;
 
   // XCD-aware order: consecutive work items land on one XCD.
   const int nb = gridDim.x;
   const int b = blockIdx.x;
   const int work = (b & 7) * (nb >> 3) + (b >> 3);
   if (work >= a.n_work) return;
-  const int g = work / a.n_tiles;
   const int nt = work % a.n_tiles;
-  const int sz = a.g.sizes[g];
-  const int e = a.g.ids[g];
-  if (sz < a.g.rows_min_tile || sz <= 0 || e < 0 || e >= a.g.E) return;
-
+  GroupRef gr;
+  if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, a.g.rows_min_tile, INT_MAX,
+                  work / a.n_tiles, gr))
+    return;
+  const int e = gr.expert;
+  const int r_begin = gr.row;
+  const int r_end = min(r_begin + gr.size, a.g.M);
+  if (r_begin >= r_end) return;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  if (tid < kWave) {
-    const int off = group_row_offset(a.g.sizes, g, tid);
-    if (tid == 0) s_off = off;
-  }
-  __syncthreads();
-  const int r_begin = s_off;
-  const int r_end = min(r_begin + sz, a.g.M);
-  if (r_begin >= r_end) return;
 
   const int N = a.g.N, K = a.g.K;
   const int i = lane & 31, h = lane >> 5;
@@ -325,7 +315,7 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   TileKArgs a;
   a.g = g;
   a.n_tiles = (g.N + kTileN - 1) / kTileN;
-  a.n_work = g.G * a.n_tiles;
+  a.n_work = (int)group_slots(g.G, g.M, g.rows_min_tile) * a.n_tiles;
   const int grid = ((a.n_work + 7) / 8) * 8;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);

@@ -120,6 +120,13 @@ BOUNDARY_CASES = {
     "tile_boundaries": (8, 96, 128, [31, 32, 33, 1, 64, 65], [0, 1, 2, 3, 4, 5], 226),
     "big_group_two_passes": (2, 64, 256, [300], [1], 300),
     "ragged_K_2880": (2, 72, 2880, [37, 3], [1, 0], 40),
+    # more than 256 group entries, so the group search walks several chunks
+    "many_groups_sparse": (300, 64, 128,
+                           [2 if g == 5 else 1 if g == 130 else 3 if g == 270 else
+                            11 if g == 299 else 0 for g in range(300)],
+                           list(range(300)), 17),
+    # more non-empty groups than rows: the later groups start past M
+    "groups_beyond_M": (12, 64, 128, [1] * 12, list(range(12)), 8),
 }
 
 
