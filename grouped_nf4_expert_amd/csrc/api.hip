@@ -191,11 +191,13 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
   const hipStream_t s = (hipStream_t)stream;
   if (run_decode) {
     DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
+    if (p.L == 0) return GNF4_ERR_UNSUPPORTED;  // this split_k leaves too much K per split
     const size_t need = decode_workspace_bytes(p, M, N);
     if (need > 0) {
       if (!ws || ws_bytes < need) {
         if (split_k > 0) return GNF4_ERR_WORKSPACE;
         p = plan_decode(M, N, K, G, 1, device_cu_count());  // no room to split: one pass
+        if (p.L == 0) return GNF4_ERR_WORKSPACE;  // K needs splitting, which needs workspace
       } else {
         if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
         if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;

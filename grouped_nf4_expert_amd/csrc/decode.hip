@@ -7,25 +7,27 @@
 // roadmap" (split-K for starved grids with a per-split work floor; one
 // universal launch rule rather than a per-shape table).
 //
-// The work is bandwidth-bound: at one row per expert every weight byte is
-// used once, so the kernel is built to have all weight bytes in flight as
-// early as possible and to spend few VALU instructions per code:
-//  * a workgroup (4 wavefronts) owns one group (expert) and a tile of weight
-//    rows; within a wavefront, a "team" of L lanes (L = 8..64, chosen from K
-//    so rows are covered with little raggedness) reads consecutive 16-byte
-//    chunks (32 codes) of one weight row, NU rows per lane;
-//  * loads are issued in the order they are consumed (group metadata, then
-//    activations, then weight rows), since vector loads complete in order;
-//    when a lane walks several chunks, the next one is prefetched while the
-//    current one is decoded;
-//  * R activation rows (a compile-time choice from the host-known rows per
-//    group) are converted to fp32 once per chunk so one decoded code feeds R
-//    multiply-adds; larger groups loop over chunks of R rows;
+// At one row per expert every weight byte is used once, so the kernel must
+// stream the weights at HBM speed while spending as few VALU instructions as
+// possible on everything else (a wave64 VALU instruction occupies its SIMD
+// for 4 cycles, so per-wavefront overhead quickly becomes the bound):
+//  * a workgroup (4 wavefronts) owns one group (expert), one K split and a
+//    tile of weight rows; within a wavefront a "team" of L lanes (L = 8..64,
+//    chosen from K so rows are covered with little raggedness) reads
+//    consecutive 16-byte chunks (32 codes) of a weight row;
+//  * each lane owns NU weight rows and `steps` chunks of each; all of its
+//    weight loads are issued at once, before anything waits, and consumed in
+//    issue order (vector loads complete in order), so a wavefront decodes
+//    its first rows while the rest are still arriving.  Few, fat wavefronts
+//    keep the per-wavefront costs (group lookup, staging, reductions) small
+//    next to the decode itself;
+//  * the activation rows of the workgroup's K range are staged once into
+//    LDS as fp32 (loads issued before the weight loads), so no wavefront
+//    loads or converts them again;
 //  * a code's level is read from a 16-entry fp32 table in LDS at an 8-byte
-//    stride (level q at bank 2q: conflict-free for any mix of codes whether
-//    the LDS has 32 or 64 banks, and the byte offset is one masked byte of a
-//    shifted packed dword), multiplied and accumulated in fp32; the block
-//    absmax is applied once per 32 codes;
+//    stride (level q at bank 2q: conflict-free for any mix of codes, and the
+//    byte offset is one masked byte of a shifted packed dword) and
+//    multiplied-added in fp32; the block absmax is applied once per 32 codes;
 //  * team partial sums are combined with a fixed butterfly and either
 //    rounded to bf16 or, when K is split across workgroups to fill the
 //    machine, written as fp32 partials that a second kernel sums in split
@@ -41,10 +43,17 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+// Staged activations per workgroup: R rows x (chunks + 1) slots of 128 bytes
+// (32 fp32) at most, i.e. 40 KB.
+constexpr int kXSlots = 320;
+constexpr int kXBatch = 2;      // 16-byte bf16 pieces per thread per staging round
+constexpr int kMaxLoads = 4;    // weight chunks in flight per lane (NU * steps)
+constexpr int kMaxSteps = 4;
 
 struct DecodeKArgs {
   GemmArgs g;
-  int S, cps, cpr, n_tiles, rows_per_block;
+  int S, cps, cpr, rows_per_block;
+  double inv_slot_div;  // 1 / slot_div, for the fused gather's row index
 };
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* out) {
@@ -105,35 +114,100 @@ __device__ __forceinline__ void load_weights(const uint8_t* wexp, const float* a
   }
 }
 
+// Activations of R rows over the workgroup's chunks [c_begin, c_begin + ncs),
+// staged in LDS as fp32.  Chunk c of row r is 32 values = eight 16-byte
+// pieces; piece p sits at 16-byte slot (r * 8 + p) * P + c with P = ncs + 1
+// (one pad slot per plane).  The lanes of a team read piece p of
+// consecutive chunks, i.e. consecutive slots: conflict-free.  A thread moves
+// up to kXBatch 16-byte bf16 pieces (= 2 fp32 pieces each) per round; the
+// first round's loads are issued before the weight loads and stored after.
 template <int R>
-__device__ __forceinline__ void load_x(const uint16_t* x, int K, const int (&xrow)[R], int c,
-                                       bool valid, uint4 (&xv)[R][4]) {
+struct XStage {
+  int ncs, plane, c_begin, per_row;
+  uint4 v[kXBatch];
+
+  __device__ __forceinline__ void init(int c_begin_, int ncs_) {
+    c_begin = c_begin_;
+    ncs = ncs_;
+    plane = ncs_ + 1;
+    per_row = ncs_ * 4;
+  }
+  __device__ __forceinline__ int row_of(int idx) const {
+    int r = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (valid && xrow[r] >= 0) {
-      const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)xrow[r] * K + 32 * (size_t)c);
+    for (int q = 1; q < R; ++q) r += idx >= q * per_row;
+    return r;
+  }
+  __device__ __forceinline__ void load(const uint16_t* x, int K, const int (&xrow)[R], int base) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[r][q] = xp[q];
-    } else {
+    for (int u = 0; u < kXBatch; ++u) {
+      const int idx = base + (int)threadIdx.x + u * kThreads;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (idx < R * per_row) {
+        const int r = row_of(idx);
+        const int rem = idx - r * per_row;
+        int src = -1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[r][q] = make_uint4(0, 0, 0, 0);
+        for (int rr = 0; rr < R; ++rr)
+          if (rr == r) src = xrow[rr];
+        if (src >= 0)
+          v[u] = *reinterpret_cast<const uint4*>(x + (size_t)src * K + 32 * (size_t)c_begin +
+                                                 8 * rem);
+      }
     }
   }
+  __device__ __forceinline__ void store(float4* s_x, int base) const {
+#pragma unroll
+    for (int u = 0; u < kXBatch; ++u) {
+      const int idx = base + (int)threadIdx.x + u * kThreads;
+      if (idx < R * per_row) {
+        const int r = row_of(idx);
+        const int rem = idx - r * per_row;
+        const int c = rem >> 2, q = rem & 3;
+        float f[8];
+        unpack_bf16x8(v[u], f);
+        float4* dst = s_x + (r * 8 + 2 * q) * plane + c;
+        dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+        dst[plane] = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+  }
+  __device__ __forceinline__ void all(const uint16_t* x, int K, const int (&xrow)[R], float4* s_x) {
+    for (int base = 0; base < R * per_row; base += kXBatch * kThreads) {
+      load(x, K, xrow, base);
+      store(s_x, base);
+    }
+  }
+};
+
+// Workgroup barrier for LDS data only: the wavefront's LDS operations are
+// complete, global loads may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// One group, a tile of weight rows, activation rows in chunks of R.
+// q = n / d for 0 <= n < 2^31, 1 <= d < 2^31, from a double estimate.
+__device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
+  int q = (int)((double)n * inv_d);
+  if ((long long)(q + 1) * d <= n) ++q;
+  if ((long long)q * d > n) --q;
+  return q;
+}
+
+// One group, one K split, a tile of weight rows; activation rows in chunks
+// of R (the weights stay in registers across chunks).
 //
 // Vector-memory loads complete in issue order, so the order of issue is the
-// schedule: (1) the group metadata (sizes of the preceding groups, and the
-// slot table when the gather is fused) from L2, (2) the activations of the
-// first chunk, (3) its NU weight rows, then per chunk the next chunk's
-// activations and weights before the current chunk is decoded -- each row's
-// arithmetic waits only for its own weight bytes.
-template <int L, int NU, int R, bool MULTI>
+// schedule: (1) the group metadata (group sizes and expert ids, and the slot
+// table when the gather is fused), (2) the first row chunk's activations,
+// (3) every weight chunk of the lane, step by step; the decode then consumes
+// the weights in the same order.
+template <int L, int NU, int R, int STEPS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
   __shared__ float s_lut[32];
+  extern __shared__ float4 s_x[];
   constexpr int RPW = kWave / L;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const bool gather = a.g.slots != nullptr;
@@ -145,44 +219,65 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   GroupRef gr;
   if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y, gr))
     return;
-  const int tile = blockIdx.x % a.n_tiles;
-  const int s = blockIdx.x / a.n_tiles;
+  const int s = blockIdx.z;
   const int team = lane / L, tl = lane % L;
   const int N = a.g.N, K = a.g.K;
-  const int n_base = tile * a.rows_per_block + wave * (RPW * NU) + team * NU;
+  const int n_base = blockIdx.x * a.rows_per_block + wave * (RPW * NU) + team * NU;
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)gr.expert * N * row_bytes;
   const float* aexp = a.g.absmax + (size_t)gr.expert * N * bpr;
   const int c_begin = s * a.cps;
   const int c_end = min(c_begin + a.cps, a.cpr);
-  const int c_first = c_begin + tl;
+  const int ncs = max(c_end - c_begin, 0);
+  const int plane = ncs + 1;
   // every wavefront writes the same values before its own reads; LDS
   // operations of one wavefront complete in order, so no barrier is needed
   const float* lut = s_lut;
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const int r_begin = gr.row;
   const int r_end = min(r_begin + gr.size, a.g.M);
-  __builtin_amdgcn_wave_barrier();
+  const int slot_lim = a.g.T * a.g.slot_div;
 
-  for (int r0 = r_begin; r0 < r_end; r0 += R) {
-    // source activation row of each of the R output rows (-1: skip the row)
-    int xrow[R];
+  // source activation row of each of the R rows of a chunk (-1: skip)
+  int xrow[R];
+  auto rows_of = [&](int r0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = r0 + r;
       xrow[r] = row < r_end ? row : -1;
       if (gather && row < r_end) {
         const int slot = slots_in_lanes ? __builtin_amdgcn_readlane(my_slot, row) : a.g.slots[row];
-        xrow[r] = (slot >= 0 && slot < a.g.T * a.g.slot_div) ? slot / a.g.slot_div : -1;
+        xrow[r] = (slot >= 0 && slot < slot_lim) ? div_slot(slot, a.g.slot_div, a.inv_slot_div) : -1;
       }
     }
-    // (2) + (3): first chunk's activations, then its weights
-    uint4 xv[R][4];
-    load_x<R>(a.g.x, K, xrow, c_first, c_first < c_end, xv);
-    uint4 wq[NU];
-    float av[NU];
-    load_weights<NU>(wexp, aexp, row_bytes, bpr, N, n_base, c_first, c_first < c_end, wq, av);
+  };
+
+  // (2) + (3): the first chunk's activations, then every weight chunk
+  rows_of(r_begin);
+  XStage<R> stage;
+  stage.init(c_begin, ncs);
+  stage.load(a.g.x, K, xrow, 0);
+  uint4 wq[STEPS][NU];
+  float av[STEPS][NU];
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int c = c_begin + tl + st * L;
+    load_weights<NU>(wexp, aexp, row_bytes, bpr, N, n_base, c, c < c_end, wq[st], av[st]);
+  }
+  stage.store(s_x, 0);
+  for (int base = kXBatch * kThreads; base < R * stage.per_row; base += kXBatch * kThreads) {
+    stage.load(a.g.x, K, xrow, base);
+    stage.store(s_x, base);
+  }
+
+  for (int r0 = r_begin; r0 < r_end; r0 += R) {
+    if (r0 != r_begin) {
+      lds_barrier();  // every wavefront is done with the previous chunk
+      rows_of(r0);
+      stage.all(a.g.x, K, xrow, s_x);
+    }
+    lds_barrier();
 
     float acc[NU][R];
 #pragma unroll
@@ -190,35 +285,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[j][r] = 0.0f;
 
-    // MULTI: a lane sees more than one chunk per row, so the next chunk is
-    // prefetched; otherwise the loop body runs at most once and carries no
-    // prefetch registers.
-    for (int c = c_first; c < c_end; c += L) {
-      const bool more = MULTI && c + L < c_end;
-      uint4 xn[R][4];
-      uint4 wn[NU];
-      float an[NU];
-      if (MULTI) {
-        load_x<R>(a.g.x, K, xrow, c + L, more, xn);
-        load_weights<NU>(wexp, aexp, row_bytes, bpr, N, n_base, c + L, more, wn, an);
-      }
-      float xs[R][32];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+    for (int st = 0; st < STEPS; ++st) {
+      const int c = c_begin + tl + st * L;
+      if (c >= c_end) continue;
+      float pr[NU][R];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) unpack_bf16x8(xv[r][q], &xs[r][8 * q]);
+      for (int j = 0; j < NU; ++j)
 #pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        float pr[R];
+        for (int r = 0; r < R; ++r) pr[j][r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) pr[r] = 0.0f;
-        const uint32_t d[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
+      for (int w = 0; w < 4; ++w) {
+        // the 8 activations of weight dword w, shared by the NU rows
+        float xw[R][8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int r = 0; r < R; ++r) {
+          const float4* src = s_x + (r * 8 + 2 * w) * plane + (c - c_begin);
+          const float4 lo = src[0], hi = src[plane];
+          xw[r][0] = lo.x; xw[r][1] = lo.y; xw[r][2] = lo.z; xw[r][3] = lo.w;
+          xw[r][4] = hi.x; xw[r][5] = hi.y; xw[r][6] = hi.z; xw[r][7] = hi.w;
+        }
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+          const uint32_t d = w == 0 ? wq[st][j].x : w == 1 ? wq[st][j].y
+                           : w == 2 ? wq[st][j].z : wq[st][j].w;
           // LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
           // byte b hold its high code; after a left shift by 3, its low code.
-          const uint32_t dh = d[w] >> 1;
-          const uint32_t dl = d[w] << 3;
+          const uint32_t dh = d >> 1;
+          const uint32_t dl = d << 3;
           uint32_t oh[4], ol[4];
           oh[0] = byte_and<0>(dh, 0x78u);
           oh[1] = byte_and<1>(dh, 0x78u);
@@ -232,27 +326,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
           for (int b = 0; b < 4; ++b) {
             const float vh = lut_at(lut, oh[b]);
             const float vl = lut_at(lut, ol[b]);
-            const int k = 8 * w + 2 * b;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-              pr[r] = fmaf(xs[r][k], vh, pr[r]);
-              pr[r] = fmaf(xs[r][k + 1], vl, pr[r]);
+              pr[j][r] = fmaf(xw[r][2 * b], vh, pr[j][r]);
+              pr[j][r] = fmaf(xw[r][2 * b + 1], vl, pr[j][r]);
             }
           }
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[j][r] = fmaf(av[j], pr[r], acc[j][r]);
       }
-      if (!MULTI) break;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int j = 0; j < NU; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xv[r][q] = xn[r][q];
-#pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        wq[j] = wn[j];
-        av[j] = an[j];
-      }
+        for (int r = 0; r < R; ++r) acc[j][r] = fmaf(av[st][j], pr[j][r], acc[j][r]);
     }
 
 #pragma unroll
@@ -300,13 +385,50 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
   }
 }
 
+template <int L, int NU, int R, int STEPS>
+hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.n_tiles, (unsigned)group_slots(a.g.G, a.g.M, 1), (unsigned)p.S);
+  const size_t lds = (size_t)R * (size_t)(p.cps + 1) * 128;
+  hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS>), grid, dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+// rows per lane times activation rows at most kMaxLoads (accumulators)
+template <int L, int NU, int STEPS>
+hipError_t launch_R(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if constexpr (NU * 4 <= kMaxLoads)
+    if (p.R == 4) return launch_one<L, NU, 4, STEPS>(a, p, stream);
+  if constexpr (NU * 2 <= kMaxLoads)
+    if (p.R == 2) return launch_one<L, NU, 2, STEPS>(a, p, stream);
+  if (p.R == 1) return launch_one<L, NU, 1, STEPS>(a, p, stream);
+  return hipErrorInvalidValue;
+}
+
+// (NU, steps) pairs with NU * steps <= kMaxLoads
+template <int L>
+hipError_t launch_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  switch (p.steps * 16 + p.NU) {
+    case 16 + 4: return launch_R<L, 4, 1>(a, p, stream);
+    case 16 + 2: return launch_R<L, 2, 1>(a, p, stream);
+    case 16 + 1: return launch_R<L, 1, 1>(a, p, stream);
+    case 32 + 2: return launch_R<L, 2, 2>(a, p, stream);
+    case 32 + 1: return launch_R<L, 1, 2>(a, p, stream);
+    case 48 + 1: return launch_R<L, 1, 3>(a, p, stream);
+    case 64 + 1: return launch_R<L, 1, 4>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Team width for a split of cps chunks: the widest of 64/32/16/8 lanes whose
+// steps (at most kMaxSteps) leave at most 1/8 of the chunk slots idle, else
+// the one with the least idle share; 0 if no width needs <= kMaxSteps steps.
 int pick_lanes(int cps) {
-  // largest team that covers the split's chunks with <= 1/8 idle slots
   const int cands[4] = {64, 32, 16, 8};
-  int best = 8;
+  int best = 0;
   double best_waste = 2.0;
   for (int L : cands) {
     const int steps = (cps + L - 1) / L;
+    if (steps > kMaxSteps) continue;
     const double waste = (double)(steps * L - cps) / (double)(steps * L);
     if (waste <= 0.125) return L;
     if (waste < best_waste) {
@@ -317,89 +439,69 @@ int pick_lanes(int cps) {
   return best;
 }
 
-template <int L, int NU, bool MULTI>
-hipError_t launch_LNM(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.n_tiles * p.S), (unsigned)group_slots(a.g.G, a.g.M, 1));
-  switch (p.R) {
-    case 4: hipLaunchKernelGGL((decode_kernel<L, NU, 4, MULTI>), grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<L, NU, 2, MULTI>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<L, NU, 1, MULTI>), grid, dim3(kThreads), 0, stream, a); break;
-  }
-  return hipGetLastError();
-}
-
-template <int L, int NU>
-hipError_t launch_LN(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
-  return p.cps > L ? launch_LNM<L, NU, true>(a, p, stream) : launch_LNM<L, NU, false>(a, p, stream);
-}
-
-template <int L>
-hipError_t launch_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
-  switch (p.NU) {
-#ifdef GNF4_TUNING
-    case 8: return launch_LN<L, 8>(a, p, stream);
-#endif
-    case 4: return launch_LN<L, 4>(a, p, stream);
-    case 2: return launch_LN<L, 2>(a, p, stream);
-    default: return launch_LN<L, 1>(a, p, stream);
-  }
-}
-
 }  // namespace
 
+// Launch rule (host-known sizes only).  Rows per pass R from the rows per
+// group; for each K split S (1 first, more only while a split keeps two team
+// steps per lane) the team width L and steps follow from the split's chunks,
+// and the rows per lane NU is the largest with NU * steps <= 4 and
+// NU * R <= 4 that still gives two wavefronts per SIMD; a split must fit its
+// activations in LDS.
 static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, int split_k,
                                    int num_cus) {
   const int cpr = (int)(K / 32);
   const int64_t g_eff = G < M ? G : M;
-  const int64_t target = 2LL * num_cus;  // workgroups that keep every CU busy
-  // rows per group the host can infer: M rows over at most min(G, M) groups
+  const int64_t target_waves = 8LL * num_cus;  // two per SIMD
   const double rows_per_group = (double)M / (double)(g_eff > 0 ? g_eff : 1);
-  const int R = rows_per_group <= 1.5 ? 1 : (rows_per_group <= 3.0 ? 2 : 4);
-  DecodePlan best{};
-  int64_t best_blocks = -1;
-  const int s_cands[4] = {1, 2, 4, 8};
-  for (int si = 0; si < 4; ++si) {
-    const int S = split_k > 0 ? split_k : s_cands[si];
-    if (split_k <= 0 && si > 0) {
-      // split only when it keeps at least two full team steps per split
-      const int cps_try = (cpr + S - 1) / S;
-      if (cps_try < 2 * pick_lanes(cps_try)) break;
-    }
-    const int cps = (cpr + S - 1) / S;
-    const int L = pick_lanes(cps);
-    // Two weight rows per lane; four when two would launch more wavefronts
-    // than the dispatcher places in about a microsecond (8192); one only to
-    // fill a starved machine.
-    const int64_t waves_nu2 = g_eff * S * ((N + (kWave / L) * 2 - 1) / ((kWave / L) * 2));
-    const int nus[3] = {waves_nu2 > 8192 ? 4 : 2, waves_nu2 > 8192 ? 2 : 1, 1};
-    for (int ni = 0; ni < 3; ++ni) {
-      DecodePlan p;
-      p.L = L;
-      p.NU = nus[ni];
-      p.R = R;
-      p.S = S;
-      p.cps = cps;
-      p.rows_per_block = kWaves * (kWave / L) * p.NU;
-      p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
-      const int64_t blocks = g_eff * p.n_tiles * S;
-      if (blocks >= target) return p;
-      if (blocks > best_blocks) {
-        best_blocks = blocks;
-        best = p;
+  const int R0 = rows_per_group <= 1.5 ? 1 : (rows_per_group <= 3.0 ? 2 : 4);
+  for (int R = R0; R >= 1; R /= 2) {
+    DecodePlan best{};
+    int64_t best_waves = -1;
+    bool split_more = false;
+    for (int S = 1; S <= 16; S = split_k > 0 ? 17 : 2 * S) {
+      if (split_k > 0) S = split_k;
+      const int cps = (cpr + S - 1) / S;
+      if (R * (cps + 1) > kXSlots) continue;
+      const int L = pick_lanes(cps);
+      if (L == 0) continue;
+      if (split_more && cps < 2 * L) break;
+      split_more = true;
+      const int steps = (cps + L - 1) / L;
+      for (int NU = kMaxLoads; NU >= 1; NU /= 2) {
+        if (NU * steps > kMaxLoads || NU * R > kMaxLoads) continue;
+        DecodePlan p{};
+        p.L = L;
+        p.NU = NU;
+        p.R = R;
+        p.S = S;
+        p.cps = cps;
+        p.steps = steps;
+        p.rows_per_block = kWaves * (kWave / L) * NU;
+        p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
+        const int64_t waves = g_eff * p.n_tiles * S * kWaves;
+        if (waves >= target_waves) return p;
+        if (waves > best_waves) {
+          best_waves = waves;
+          best = p;
+        }
       }
     }
-    if (split_k > 0) break;
+    if (best_waves >= 0) return best;
   }
-  return best;
+  return DecodePlan{};  // L == 0: no split of K fits
 }
 
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, int num_cus) {
   DecodePlan p = plan_decode_rule(M, N, K, G, split_k, num_cus);
-#ifdef GNF4_TUNING  // experiment builds only: override the launch rule
+#ifdef GNF4_TUNING  // experiment builds only: override the rows per lane
   if (const char* v = getenv("GNF4_TUNE_NU")) {
-    p.NU = atoi(v);
-    p.rows_per_block = kWaves * (kWave / p.L) * p.NU;
-    p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
+    const int nu = atoi(v);
+    if (p.L != 0 && (nu == 1 || nu == 2 || nu == 4) && nu * p.steps <= kMaxLoads &&
+        nu * p.R <= kMaxLoads) {
+      p.NU = nu;
+      p.rows_per_block = kWaves * (kWave / p.L) * p.NU;
+      p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
+    }
   }
 #endif
   return p;
@@ -415,14 +517,15 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
   a.S = p.S;
   a.cps = p.cps;
   a.cpr = g.K / 32;
-  a.n_tiles = p.n_tiles;
   a.rows_per_block = p.rows_per_block;
+  a.inv_slot_div = 1.0 / (double)(g.slot_div > 0 ? g.slot_div : 1);
   hipError_t err;
   switch (p.L) {
     case 64: err = launch_L<64>(a, p, stream); break;
     case 32: err = launch_L<32>(a, p, stream); break;
     case 16: err = launch_L<16>(a, p, stream); break;
-    default: err = launch_L<8>(a, p, stream); break;
+    case 8: err = launch_L<8>(a, p, stream); break;
+    default: return hipErrorInvalidValue;
   }
   if (err != hipSuccess || p.S == 1) return err;
   const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)group_slots(g.G, g.M, 1));

@@ -196,6 +196,7 @@ struct DecodePlan {
   int R;        // activation rows per pass over a weight tile
   int S;        // K splits
   int cps;      // 32-code chunks per split
+  int steps;    // chunks per lane and weight row: ceil(cps / L)
   int n_tiles;  // weight-row tiles per group
   int rows_per_block;
 };

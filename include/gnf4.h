@@ -180,9 +180,13 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
  * deterministic run to run.
  *
  * Limits: M >= 0, G >= 0 (either 0: nothing to do), E, N >= 1, K >= 64 with
- * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call.
- * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE,
- * GNF4_ERR_HIP.
+ * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call,
+ * G < 65536.  The decode path keeps one K split of an activation row in LDS,
+ * at most 319 chunks of 32 (K <= 10208 unsplit); a larger K is split across
+ * workgroups, which needs the workspace.
+ * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE
+ * (also: K too large to run unsplit and no workspace given),
+ * GNF4_ERR_UNSUPPORTED (a limit above exceeded), GNF4_ERR_HIP.
  */
 size_t gnf4_grouped_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);
 
@@ -197,7 +201,8 @@ gnf4_status gnf4_grouped_gemm(const uint16_t* x_sorted, const uint8_t* packed,
  * tests and tuning.  `path`: 0 = automatic (same as gnf4_grouped_gemm),
  * 1 = every group on the decode path, 2 = every group on the tile path.
  * `split_k`: 0 = automatic, else the number of K splits of the decode path
- * (1..16; needs workspace of gnf4_grouped_gemm_workspace_size_ex()).
+ * (1..16; needs workspace of gnf4_grouped_gemm_workspace_size_ex();
+ * GNF4_ERR_UNSUPPORTED if a split would hold more than 319 chunks of 32).
  * Results of all paths satisfy the same tolerance contract.
  */
 size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
