@@ -58,6 +58,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch every kernel from the host instead of replaying a HIP graph")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="distinct weight sets cycled by the steps (0 = enough for >= 1 GiB)")
+    ap.add_argument("--dominant-only", action="store_true",
+                    help="only launch the dominant kernel (for counter collection), print its timing")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB --steps times "
+                         "(calibrates the HBM byte counters)")
+    ap.add_argument("--summarize", default="",
+                    help="print a summary of the rocprofv3 CSV output in this directory and exit")
     return ap.parse_args()
 
 
@@ -81,7 +90,7 @@ def capture(fn):
     return g
 
 
-def build_layers(wl, L, dev):
+def build_layers(wl, L, dev, first_layer=0):
     import torch
     from grouped_nf4_expert_amd import gnf4
     from grouped_nf4_expert_amd import workloads as wls
@@ -89,7 +98,7 @@ def build_layers(wl, L, dev):
     Kg, Ng = wl.gemm("gate_up")
     Kd, Nd = wl.gemm("down")
     layers = []
-    for li in range(L):
+    for li in range(first_layer, first_layer + L):
         ly = Layer()
         ly.pg = torch.empty((wl.E, Ng, Kg // 2), dtype=torch.uint8, device=dev)
         ly.ag = torch.empty((wl.E, Ng, Kg // 64), dtype=torch.float32, device=dev)
@@ -241,8 +250,77 @@ def time_cells(path, dev):
     out.close()
 
 
+KERNEL_SOURCES = ("grouped_nf4_expert_amd/csrc/decode.hip",
+                  "grouped_nf4_expert_amd/csrc/gnf4_internal.h")
+
+
+def kernel_digest():
+    """Short sha256 over the sources of the decode kernel and its launch rule:
+    a stored counter reading is only valid for the code it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(wl_name):
+    return os.path.join(ROOT, "profiles", f"decode_gate_up_{wl_name}_counters.txt")
+
+
+def read_traffic(wl_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or the kernel changed since."""
+    path = traffic_file(wl_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_digest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(d):
+    """Text summary of rocprofv3 CSV output (kernel stats and/or counters)."""
+    import csv
+    import glob
+    import re
+
+    def short(name):
+        m = re.search(r"gnf4::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
+        return (m.group(1) + (m.group(2) or "")) if m else name[:60]
+
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel statistics ({os.path.relpath(f, d)})")
+        print(f"{'kernel':<48} {'calls':>7} {'avg us':>9} {'min us':>9} {'max us':>9} {'total %':>8}")
+        for r in csv.DictReader(open(f)):
+            print(f"{short(r['Name']):<48} {int(r['Calls']):>7} {float(r['AverageNs'])/1e3:>9.3f} "
+                  f"{float(r['MinNs'])/1e3:>9.3f} {float(r['MaxNs'])/1e3:>9.3f} "
+                  f"{float(r['Percentage']):>8.2f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        print(f"# counters per dispatch, averaged per kernel ({os.path.relpath(f, d)})")
+        agg = {}
+        for r in csv.DictReader(open(f)):
+            k = (short(r["Kernel_Name"]), r["Counter_Name"])
+            agg.setdefault(k, []).append(float(r["Counter_Value"]))
+        for (kn, cn), v in sorted(agg.items()):
+            print(f"{kn:<48} {cn:<22} dispatches={len(v):>5} mean={sum(v)/len(v):.1f}")
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
@@ -254,66 +332,103 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     gnf4.library()
     dev = torch.device("cuda:0")
+
+    if args.copy_mb:
+        # calibration for the HBM byte counters: a plain copy of known size
+        n = args.copy_mb << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mb, "reps": args.steps}))
+        return
+
     wl = wls.WORKLOADS[args.workload]
     L = args.layers or wl.layers
-    print(f"[bench] building {L} layers of {wl.name}", file=sys.stderr, flush=True)
-    layers = build_layers(wl, L, dev)
-
     Kg, Ng = wl.gemm("gate_up")
     Kd, Nd = wl.gemm("down")
-    for ly in layers:
-        run_layer(wl, ly)
+    g_est = min(wl.E, wl.M)
+    step_est = L * (gemm_bytes(g_est, wl.M, Ng, Kg) + gemm_bytes(g_est, wl.M, Nd, Kd))
+    # enough distinct weight sets that the steps cycle through >= 1 GiB of
+    # expert bytes, four times the 256 MB Infinity Cache: every step streams
+    # its weights from HBM
+    n_sets = args.sets or max(1, min(8, -(-(1 << 30) // step_est)))
+    print(f"[bench] building {n_sets} x {L} layers of {wl.name}", file=sys.stderr, flush=True)
+    sets = [build_layers(wl, L, dev, first_layer=k * L) for k in range(n_sets)]
+
+    for layers in sets:
+        for ly in layers:
+            run_layer(wl, ly)
     torch.cuda.synchronize()
-    touched = [int(ly.route.result.num_groups.cpu()[0]) for ly in layers]
-    step_bytes = sum(route_bytes(wl.T, wl.E, wl.top_k) +
-                     gemm_bytes(n, wl.M, Ng, Kg) + gemm_bytes(n, wl.M, Nd, Kd) for n in touched)
-    dom_bytes = [gemm_bytes(n, wl.M, Ng, Kg) for n in touched]
+    touched = [[int(ly.route.result.num_groups.cpu()[0]) for ly in layers] for layers in sets]
+    set_bytes = [sum(route_bytes(wl.T, wl.E, wl.top_k) + gemm_bytes(n, wl.M, Ng, Kg) +
+                     gemm_bytes(n, wl.M, Nd, Kd) for n in t) for t in touched]
+    dom_bytes = [gemm_bytes(n, wl.M, Ng, Kg) for t in touched for n in t]
 
-    # one step = every layer's launches, captured once as a HIP graph and
-    # replayed (the decode kernels are a few microseconds each: host launch
-    # overhead would otherwise dominate)
-    step = capture(lambda: [run_layer(wl, ly) for ly in layers]) if args.graph else None
+    flat = [ly for layers in sets for ly in layers]
 
-    def run_step():
-        if step is not None:
-            step.replay()
+    def dominant_host(reps):
+        """The gate_up GEMM launched on its own from the host, cycling every
+        layer of every set (for counter collection)."""
+        for i in range(reps):
+            gate_up(wl, flat[i % len(flat)])
+        torch.cuda.synchronize()
+
+    def dominant_timed(replays):
+        """The gate_up GEMM of every layer of every set, twice, launched back
+        to back from one HIP graph; HIP events on the launch stream bracket
+        each replay.  Per-launch duration = replay time / launches."""
+        n = 2 * len(flat)
+        g = capture(lambda: [gate_up(wl, flat[i % len(flat)]) for i in range(n)])
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(replays)]
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(replays):
+            evs[i][0].record()
+            g.replay()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) * 1e3 / n for s, e in evs]
+
+    if args.dominant_only:
+        dominant_host(max(args.steps, 1))
+        print(json.dumps({"kernel": "gate_up decode GEMM", "launches": max(args.steps, 1)}))
+        return
+
+    # one step = every layer's launches, captured once per weight set as a
+    # HIP graph and replayed (the decode kernels take microseconds: host
+    # launch overhead would otherwise dominate)
+    graphs = [capture(lambda layers=layers: [run_layer(wl, ly) for ly in layers])
+              if args.graph else None for layers in sets]
+
+    def run_step(i):
+        k = i % n_sets
+        if graphs[k] is not None:
+            graphs[k].replay()
         else:
-            for ly in layers:
+            for ly in sets[k]:
                 run_layer(wl, ly)
 
-    for _ in range(args.warmup):
-        run_step()
+    for i in range(args.warmup):
+        run_step(i)
     # timed region: exactly `steps` steps, synchronised on both sides
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step()
+    for i in range(args.steps):
+        run_step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    value = step_bytes / (ms * 1e-3) / 1e9
+    timed_bytes = sum(set_bytes[i % n_sets] for i in range(args.steps))
+    value = timed_bytes / ((t1 - t0)) / 1e9
 
-    # dominant kernel: the gate_up GEMM of every layer launched back to back
-    # (one graph), HIP events on the same stream around each replay
-    def gate_up_only():
-        for ly in layers:
-            gate_up(wl, ly)
-    dom = capture(gate_up_only) if args.graph else None
-    reps = max(args.steps, 10)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for i in range(reps):
-        evs[i][0].record()
-        if dom is not None:
-            dom.replay()
-        else:
-            gate_up_only()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    dur_us = [s.elapsed_time(e) * 1e3 / L for s, e in evs]
-    avg_us = float(np.median(dur_us))
+    dur_us = dominant_timed(10)
+    avg_us = float(np.mean(dur_us))
     achieved = float(np.mean(dom_bytes)) / (avg_us * 1e-6) / 1e9
+    traffic = read_traffic(wl.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,18 +455,23 @@ def main():
             "weights": "NF4 (block 64, fp32 absmax)", "activations": "bf16",
             "global_batch": wl.T, "layers": L, "parallelism": "none (1 GPU)",
             "launch": "HIP graph per step" if args.graph else "host launches",
-            "step_bytes": step_bytes, "touched_experts_per_layer": touched,
+            "weight_sets": n_sets, "bytes_per_step": [int(b) for b in set_bytes],
+            "touched_experts_per_layer": touched[0],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode-path grouped GEMM (gate_up), launched back to back over the layers",
+            "kernel": "decode-path grouped GEMM (gate_up, fused row gather), "
+                      f"{2 * len(flat)} launches back to back per HIP graph replay",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_us": round(avg_us, 3),
+            "median_launch_us": round(float(np.median(dur_us)), 3),
+            "launches_timed": 20 * len(flat),
             "algorithmic_bytes_per_launch": int(np.mean(dom_bytes)),
+            "kernel_source_digest": kernel_digest(),
         },
         "cpu_baseline": cpu,
     }
