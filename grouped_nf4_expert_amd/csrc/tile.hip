@@ -17,14 +17,16 @@
 // fp32 on the matrix core, and the epilogue multiplies by 2^s_n exactly and
 // rounds to bf16.
 //
-// Work layout (XCD-aware): a workgroup of 4 wavefronts owns one (group, 256
+// Work layout (XCD-aware): a workgroup of 8 wavefronts owns one (group, 256
 // output columns) tile and walks K in steps of 128 (two absmax blocks).  All
-// 4 wavefronts of one group's column tiles are dispatched to the same XCD so
-// the group's activation rows stay in that XCD's L2.  Each wavefront owns 64
-// columns (2 MFMA column tiles) for every row of the group (up to 6 row
-// tiles of 32 per pass), so every code is decoded exactly once per pass:
-//  * weights: a lane owns one weight row of each column tile and one 64-code
-//    absmax block per K step (lane half h = block h); it loads its 32 bytes
+// workgroups of one group's column tiles are dispatched to the same XCD so
+// the group's activation rows stay in that XCD's L2.  Each wavefront owns 32
+// columns (one MFMA column tile) for every row of the group (up to 6 row
+// tiles of 32 per pass), so every code is decoded exactly once per pass; one
+// column tile per wavefront keeps the registers within two wavefronts per
+// SIMD, so one wavefront's decode overlaps the other's matrix-core work:
+//  * weights: a lane owns one weight row and one 64-code absmax block per K
+//    step (lane half h = block h); it loads its 32 bytes
 //    straight from HBM into registers, builds the 16-entry fp16 table of that
 //    block (16 products, 8 packs, 8 byte-plane permutes) and decodes 8 codes
 //    per dword with v_perm_b32 byte lookups -- no LDS traffic for weights;
@@ -43,8 +45,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kTileN = 256;        // output columns per workgroup
+constexpr int kThreads = 512;      // 8 wavefronts, two per SIMD
+constexpr int kTileN = 256;        // output columns per workgroup (32 per wavefront)
 constexpr int kStepK = 128;        // K per main-loop step
 constexpr int kRowTiles = 6;       // 32-row MFMA tiles per pass
 constexpr int kPassRows = 32 * kRowTiles;
@@ -131,7 +133,7 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
 
   // XCD-aware order: consecutive work items land on one XCD.
@@ -153,17 +155,17 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
 
   const int N = a.g.N, K = a.g.K;
   const int i = lane & 31, h = lane >> 5;
-  const int n_wave = nt * kTileN + wave * 64;
-  const int nrow[2] = {n_wave + i, n_wave + 32 + i};
+  const int n_wave = nt * kTileN + wave * 32;
+  const int nrow[1] = {n_wave + i};
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
   const float* aexp = a.g.absmax + (size_t)e * N * bpr;
 
   // per-row power-of-two scale from the row's largest block absmax
-  int sexp[2];
+  int sexp[1];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < 1; ++t) {
     float m = 0.0f;
     if (nrow[t] < N) {
       const float* ar = aexp + (size_t)nrow[t] * bpr;
@@ -182,13 +184,11 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
     const int rows = min(kPassRows, r_end - p0);
     const int rt_n = (rows + 31) / 32;
 
-    float16v acc[kRowTiles][2];
+    float16v acc[kRowTiles][1];
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) acc[rt][0][v] = 0.0f;
 
     const int total_steps = n_steps + (rem_k ? 1 : 0);
 
@@ -231,12 +231,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
       }
     };
     // weight codes: lane loads block h of its two rows for a step (32 bytes each)
-    uint4 wc[2][2];
-    float wa[2];
+    uint4 wc[1][2];
+    float wa[1];
     auto load_w = [&](int step) {
       const int blk = 2 * step + h;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 1; ++t) {
         wc[t][0] = wc[t][1] = make_uint4(0, 0, 0, 0);
         wa[t] = 0.0f;
         if (nrow[t] < N && blk < bpr) {
@@ -253,33 +253,26 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
     for (int step = 0; step < total_steps; ++step) {
       const int buf = step & 1;
       store_x(buf);
-      uint4 cw[2][2] = {{wc[0][0], wc[0][1]}, {wc[1][0], wc[1][1]}};
-      const float ca[2] = {wa[0], wa[1]};
+      uint4 cw[1][2] = {{wc[0][0], wc[0][1]}};
+      const float ca[1] = {wa[0]};
       __syncthreads();
       if (step + 1 < total_steps) {
         load_x(step + 1);
         load_w(step + 1);
       }
       const Table tab0 = make_table(ldexpf(ca[0], -sexp[0]));
-      const Table tab1 = make_table(ldexpf(ca[1], -sexp[1]));
       const bool half_step = (rem_k != 0) && (step == n_steps);  // only block 0 valid
       const _Float16* xs = &s_x[buf][0];
 #pragma unroll
       for (int sub = 0; sub < 8; ++sub) {
         const uint32_t d0 = (&cw[0][0].x)[sub];
-        const uint32_t d1 = (&cw[1][0].x)[sub];
         half8 bw0 = decode8(d0, tab0);
-        half8 bw1 = decode8(d1, tab1);
-        if (half_step && h) {  // lanes of the missing block contribute zero
-          bw0 = (half8){};
-          bw1 = (half8){};
-        }
+        if (half_step && h) bw0 = (half8){};  // lanes of the missing block contribute zero
 #pragma unroll
         for (int rt = 0; rt < kRowTiles; ++rt) {
           if (rt < rt_n) {
             const half8 ax = *reinterpret_cast<const half8*>(xs + (rt * 32 + i) * kLdsRow + 64 * h + 8 * sub);
             acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bw0, acc[rt][0], 0, 0, 0);
-            acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bw1, acc[rt][1], 0, 0, 0);
           }
         }
       }
@@ -290,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileKArgs a) {
     for (int rt = 0; rt < kRowTiles; ++rt) {
       if (rt >= rt_n) continue;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 1; ++t) {
         const int n = nrow[t];
         if (n >= N) continue;
 #pragma unroll
