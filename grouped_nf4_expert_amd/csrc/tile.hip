@@ -51,7 +51,6 @@ constexpr int kStepK = 128;        // K per main-loop step
 constexpr int kRowTiles = 6;       // 32-row MFMA tiles per pass
 constexpr int kPassRows = 32 * kRowTiles;
 constexpr int kLdsRow = kStepK + 8;  // fp16 elements per staged row (padded)
-constexpr int kXChunks = kPassRows * (kStepK / 8) / kThreads;  // 16-byte loads per thread
 
 struct TileKArgs {
   GemmArgs g;
@@ -133,6 +132,137 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
   return r;
 }
 
+// Everything one pass over K needs, shared by the row-tile specialisations.
+struct PassCtx {
+  const TileKArgs* a;
+  _Float16* s_x;           // [2][kPassRows * kLdsRow]
+  const uint8_t* wrow;     // this lane's weight row (or row 0 when out of range)
+  const float* arow;       // its absmax row
+  bool n_ok;               // the lane's column exists
+  int sexp;                // its power-of-two scale exponent
+  int tid, i, h, N, K, bpr, n, p0, rows, r_end, n_steps, rem_k;
+};
+
+// q = n / d for 0 <= n < 2^31, 1 <= d < 2^31, from a double estimate.
+__device__ __forceinline__ int div_slot(int n, int d) {
+  int q = (int)((double)n / (double)d);
+  if ((long long)(q + 1) * d <= n) ++q;
+  if ((long long)q * d > n) --q;
+  return q;
+}
+
+// One pass of up to RT row tiles (RT * 32 rows) over the whole K range.  RT
+// is a compile-time constant so the row-tile loops carry no branches: every
+// MFMA of a sub-step and its A-fragment reads are issued back to back, and
+// the next sub-step's decode can overlap them.  Loads are unconditional (an
+// absent row or column reads an always-valid address) and what is absent is
+// dropped where the values are used: zero activations at staging, a zero
+// decode table for an absent weight block.
+template <int RT>
+__device__ __forceinline__ void tile_pass(const PassCtx& c) {
+  const GemmArgs& g = c.a->g;
+  constexpr int kChunks = RT;  // 16-byte x chunks per thread: RT*32 rows x 16 chunks / 512 threads
+  float16v acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[rt][v] = 0.0f;
+
+  const int total_steps = c.n_steps + (c.rem_k ? 1 : 0);
+  // source row of each staged chunk (-1: absent, staged as zeros)
+  int xsrc[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int row = (c.tid + kThreads * j) >> 4;
+    int src = -1;
+    if (row < c.rows) {
+      src = c.p0 + row;
+      if (g.slots) {
+        const int slot = g.slots[c.p0 + row];
+        src = (slot >= 0 && slot < g.T * g.slot_div) ? div_slot(slot, g.slot_div) : -1;
+      }
+    }
+    xsrc[j] = src;
+  }
+  uint4 xr[kChunks];
+  auto load_x = [&](int step) {
+    const int k0 = step * kStepK;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c16 = (c.tid + kThreads * j) & 15;
+      const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
+      xr[j] = *reinterpret_cast<const uint4*>(
+          g.x + (ok ? (size_t)xsrc[j] * c.K + k0 + 8 * c16 : 0));
+    }
+  };
+  auto store_x = [&](int buf, int step) {
+    const int k0 = step * kStepK;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int q = c.tid + kThreads * j;
+      const int row = q >> 4, c16 = q & 15;
+      const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
+      *reinterpret_cast<uint4*>(&c.s_x[buf * (kPassRows * kLdsRow) + row * kLdsRow + 8 * c16]) =
+          bf16x8_to_f16_slots(ok ? xr[j] : make_uint4(0, 0, 0, 0));
+    }
+  };
+  // weight codes: the lane's 32 bytes of block h of the step, and its absmax
+  uint4 wc[2];
+  float wa;
+  auto load_w = [&](int step) {
+    const int blk = 2 * step + c.h;
+    const bool ok = c.n_ok && blk < c.bpr;
+    const uint4* p = reinterpret_cast<const uint4*>(c.wrow + (ok ? 32 * (size_t)blk : 0));
+    wc[0] = p[0];
+    wc[1] = p[1];
+    wa = c.arow[ok ? blk : 0];
+  };
+
+  load_x(0);
+  load_w(0);
+  for (int step = 0; step < total_steps; ++step) {
+    const int buf = step & 1;
+    store_x(buf, step);
+    const uint4 cw[2] = {wc[0], wc[1]};
+    const float ca = wa;
+    const bool cok = c.n_ok && 2 * step + c.h < c.bpr;
+    __syncthreads();
+    // prefetch the next step (the last step re-reads its own data)
+    const int nxt = min(step + 1, total_steps - 1);
+    load_x(nxt);
+    load_w(nxt);
+    const Table tab = make_table(cok ? ldexpf(ca, -c.sexp) : 0.0f);
+    const _Float16* xs = c.s_x + buf * (kPassRows * kLdsRow);
+#pragma unroll
+    for (int sub = 0; sub < 8; ++sub) {
+      const half8 bw = decode8((&cw[0].x)[sub], tab);
+      half8 ax[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        ax[rt] = *reinterpret_cast<const half8*>(xs + (rt * 32 + c.i) * kLdsRow + 64 * c.h + 8 * sub);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[rt], bw, acc[rt], 0, 0, 0);
+    }
+  }
+
+  // epilogue: D[row][col], col = lane % 32, row = 8 (v / 4) + 4 h + v % 4
+  if (!c.n_ok) return;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = c.p0 + rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
+      if (row >= c.r_end) continue;
+      if (g.slots) {
+        const int slot = g.slots[row];
+        if (slot < 0 || slot >= g.T * g.slot_div) continue;
+      }
+      g.y[(size_t)row * c.N + c.n] = f32_to_bf16(ldexpf(acc[rt][v], c.sexp));
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
 
@@ -156,147 +286,50 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const int N = a.g.N, K = a.g.K;
   const int i = lane & 31, h = lane >> 5;
   const int n_wave = nt * kTileN + wave * 32;
-  const int nrow[1] = {n_wave + i};
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
   const float* aexp = a.g.absmax + (size_t)e * N * bpr;
 
   // per-row power-of-two scale from the row's largest block absmax
-  int sexp[1];
-#pragma unroll
-  for (int t = 0; t < 1; ++t) {
-    float m = 0.0f;
-    if (nrow[t] < N) {
-      const float* ar = aexp + (size_t)nrow[t] * bpr;
-      for (int bk = h; bk < bpr; bk += 2) m = fmaxf(m, ar[bk]);
-    }
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    int ex = 0;
-    (void)frexpf(m, &ex);
-    sexp[t] = ex;
+  const int n = n_wave + i;
+  const bool n_ok = n < N;
+  float m = 0.0f;
+  if (n_ok) {
+    const float* ar = aexp + (size_t)n * bpr;
+    for (int bk = h; bk < bpr; bk += 2) m = fmaxf(m, ar[bk]);
   }
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  int sexp = 0;
+  (void)frexpf(m, &sexp);
 
-  const int n_steps = K / kStepK;
-  const int rem_k = K - n_steps * kStepK;  // a final 64-wide step when K % 128 == 64
-
+  PassCtx c;
+  c.a = &a;
+  c.s_x = &s_x[0][0];
+  c.wrow = wexp + (n_ok ? (size_t)n * row_bytes : 0);
+  c.arow = aexp + (n_ok ? (size_t)n * bpr : 0);
+  c.n_ok = n_ok;
+  c.sexp = sexp;
+  c.tid = tid;
+  c.i = i;
+  c.h = h;
+  c.N = N;
+  c.K = K;
+  c.bpr = bpr;
+  c.n = n;
+  c.r_end = r_end;
+  c.n_steps = K / kStepK;
+  c.rem_k = K - c.n_steps * kStepK;  // a final 64-wide step when K % 128 == 64
   for (int p0 = r_begin; p0 < r_end; p0 += kPassRows) {
-    const int rows = min(kPassRows, r_end - p0);
-    const int rt_n = (rows + 31) / 32;
-
-    float16v acc[kRowTiles][1];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[rt][0][v] = 0.0f;
-
-    const int total_steps = n_steps + (rem_k ? 1 : 0);
-
-    // x staging: thread owns 16-byte chunks q = tid + 256 * j of the pass
-    // tile (row q / 16, K slice 8 * (q % 16))
-    // source activation row of each staged chunk (fused gather: via the
-    // slot table; -1 = row not present, staged as zeros)
-    int xsrc[kXChunks];
-#pragma unroll
-    for (int j = 0; j < kXChunks; ++j) {
-      const int row = (tid + kThreads * j) >> 4;
-      int src = -1;
-      if (row < rows) {
-        src = p0 + row;
-        if (a.g.slots) {
-          const int slot = a.g.slots[p0 + row];
-          src = (slot >= 0 && slot < a.g.T * a.g.slot_div) ? slot / a.g.slot_div : -1;
-        }
-      }
-      xsrc[j] = src;
-    }
-    uint4 xr[kXChunks];
-    auto load_x = [&](int step) {
-      const int k0 = step * kStepK;
-#pragma unroll
-      for (int j = 0; j < kXChunks; ++j) {
-        const int c16 = (tid + kThreads * j) & 15;
-        xr[j] = make_uint4(0, 0, 0, 0);
-        if (xsrc[j] >= 0 && k0 + 8 * c16 < K)
-          xr[j] = *reinterpret_cast<const uint4*>(a.g.x + (size_t)xsrc[j] * K + k0 + 8 * c16);
-      }
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < kXChunks; ++j) {
-        const int q = tid + kThreads * j;
-        const int row = q >> 4, c16 = q & 15;
-        if (row < rows)
-          *reinterpret_cast<uint4*>(&s_x[buf][row * kLdsRow + 8 * c16]) = bf16x8_to_f16_slots(xr[j]);
-      }
-    };
-    // weight codes: lane loads block h of its two rows for a step (32 bytes each)
-    uint4 wc[1][2];
-    float wa[1];
-    auto load_w = [&](int step) {
-      const int blk = 2 * step + h;
-#pragma unroll
-      for (int t = 0; t < 1; ++t) {
-        wc[t][0] = wc[t][1] = make_uint4(0, 0, 0, 0);
-        wa[t] = 0.0f;
-        if (nrow[t] < N && blk < bpr) {
-          const uint4* p = reinterpret_cast<const uint4*>(wexp + (size_t)nrow[t] * row_bytes + 32 * (size_t)blk);
-          wc[t][0] = p[0];
-          wc[t][1] = p[1];
-          wa[t] = aexp[(size_t)nrow[t] * bpr + blk];
-        }
-      }
-    };
-
-    load_x(0);
-    load_w(0);
-    for (int step = 0; step < total_steps; ++step) {
-      const int buf = step & 1;
-      store_x(buf);
-      uint4 cw[1][2] = {{wc[0][0], wc[0][1]}};
-      const float ca[1] = {wa[0]};
-      __syncthreads();
-      if (step + 1 < total_steps) {
-        load_x(step + 1);
-        load_w(step + 1);
-      }
-      const Table tab0 = make_table(ldexpf(ca[0], -sexp[0]));
-      const bool half_step = (rem_k != 0) && (step == n_steps);  // only block 0 valid
-      const _Float16* xs = &s_x[buf][0];
-#pragma unroll
-      for (int sub = 0; sub < 8; ++sub) {
-        const uint32_t d0 = (&cw[0][0].x)[sub];
-        half8 bw0 = decode8(d0, tab0);
-        if (half_step && h) bw0 = (half8){};  // lanes of the missing block contribute zero
-#pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
-          if (rt < rt_n) {
-            const half8 ax = *reinterpret_cast<const half8*>(xs + (rt * 32 + i) * kLdsRow + 64 * h + 8 * sub);
-            acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax, bw0, acc[rt][0], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // epilogue: D[row][col], col = lane % 32, row = 8 (v / 4) + 4 h + v % 4
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      if (rt >= rt_n) continue;
-#pragma unroll
-      for (int t = 0; t < 1; ++t) {
-        const int n = nrow[t];
-        if (n >= N) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = p0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (row >= r_end) continue;
-          if (a.g.slots) {
-            const int slot = a.g.slots[row];
-            if (slot < 0 || slot >= a.g.T * a.g.slot_div) continue;
-          }
-          a.g.y[(size_t)row * N + n] = f32_to_bf16(ldexpf(acc[rt][t][v], sexp[t]));
-        }
-      }
+    c.p0 = p0;
+    c.rows = min(kPassRows, r_end - p0);
+    switch ((c.rows + 31) / 32) {
+      case 1: tile_pass<1>(c); break;
+      case 2: tile_pass<2>(c); break;
+      case 3: tile_pass<3>(c); break;
+      case 4: tile_pass<4>(c); break;
+      case 5: tile_pass<5>(c); break;
+      default: tile_pass<6>(c); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
