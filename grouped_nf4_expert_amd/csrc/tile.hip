@@ -37,6 +37,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 #include "gnf4_internal.h"
 
 namespace gnf4 {
@@ -184,18 +186,27 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
     }
     xsrc[j] = src;
   }
-  uint4 xr[kChunks];
-  auto load_x = [&](int step) {
+  // Two register sets (activations and weights) alternate between steps so
+  // every load is issued two steps before it is used: step s computes from
+  // LDS buffer s % 2, then stages step s + 1's activations (loaded during
+  // step s - 1) into the other buffer; one barrier per step.  The step loop
+  // is unrolled by two so the register sets are static.
+  uint4 xr[2][kChunks];
+  uint4 wc[2][2];
+  float wa[2];
+  auto load_x = [&](auto slot_c, int step) {
+    constexpr int sl = decltype(slot_c)::value;
     const int k0 = step * kStepK;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
       const int c16 = (c.tid + kThreads * j) & 15;
       const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
-      xr[j] = *reinterpret_cast<const uint4*>(
+      xr[sl][j] = *reinterpret_cast<const uint4*>(
           g.x + (ok ? (size_t)xsrc[j] * c.K + k0 + 8 * c16 : 0));
     }
   };
-  auto store_x = [&](int buf, int step) {
+  auto store_x = [&](auto slot_c, int buf, int step) {
+    constexpr int sl = decltype(slot_c)::value;
     const int k0 = step * kStepK;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
@@ -203,36 +214,33 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
       const int row = q >> 4, c16 = q & 15;
       const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
       *reinterpret_cast<uint4*>(&c.s_x[buf * (kPassRows * kLdsRow) + row * kLdsRow + 8 * c16]) =
-          bf16x8_to_f16_slots(ok ? xr[j] : make_uint4(0, 0, 0, 0));
+          bf16x8_to_f16_slots(ok ? xr[sl][j] : make_uint4(0, 0, 0, 0));
     }
   };
   // weight codes: the lane's 32 bytes of block h of the step, and its absmax
-  uint4 wc[2];
-  float wa;
-  auto load_w = [&](int step) {
+  auto load_w = [&](auto slot_c, int step) {
+    constexpr int sl = decltype(slot_c)::value;
     const int blk = 2 * step + c.h;
     const bool ok = c.n_ok && blk < c.bpr;
     const uint4* p = reinterpret_cast<const uint4*>(c.wrow + (ok ? 32 * (size_t)blk : 0));
-    wc[0] = p[0];
-    wc[1] = p[1];
-    wa = c.arow[ok ? blk : 0];
+    wc[sl][0] = p[0];
+    wc[sl][1] = p[1];
+    wa[sl] = c.arow[ok ? blk : 0];
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int last = total_steps - 1;
 
-  load_x(0);
-  load_w(0);
-  for (int step = 0; step < total_steps; ++step) {
-    const int buf = step & 1;
-    store_x(buf, step);
-    const uint4 cw[2] = {wc[0], wc[1]};
-    const float ca = wa;
+  auto do_step = [&](auto slot_c, int step) {
+    constexpr int sl = decltype(slot_c)::value;
+    using SO = std::integral_constant<int, 1 - sl>;
+    const uint4 cw[2] = {wc[sl][0], wc[sl][1]};
+    const float ca = wa[sl];
     const bool cok = c.n_ok && 2 * step + c.h < c.bpr;
-    __syncthreads();
-    // prefetch the next step (the last step re-reads its own data)
-    const int nxt = min(step + 1, total_steps - 1);
-    load_x(nxt);
-    load_w(nxt);
+    load_x(slot_c, min(step + 2, last));
+    load_w(slot_c, min(step + 2, last));
     const Table tab = make_table(cok ? ldexpf(ca, -c.sexp) : 0.0f);
-    const _Float16* xs = c.s_x + buf * (kPassRows * kLdsRow);
+    const _Float16* xs = c.s_x + sl * (kPassRows * kLdsRow);
 #pragma unroll
     for (int sub = 0; sub < 8; ++sub) {
       const half8 bw = decode8((&cw[0].x)[sub], tab);
@@ -244,20 +252,45 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
       for (int rt = 0; rt < RT; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[rt], bw, acc[rt], 0, 0, 0);
     }
+    if (step < last) {
+      store_x(SO{}, 1 - sl, step + 1);
+      __syncthreads();
+    }
+  };
+
+  load_x(S0{}, 0);
+  load_w(S0{}, 0);
+  load_x(S1{}, min(1, last));
+  load_w(S1{}, min(1, last));
+  store_x(S0{}, 0, 0);
+  __syncthreads();
+  for (int step = 0; step < total_steps; step += 2) {
+    do_step(S0{}, step);
+    if (step + 1 < total_steps) do_step(S1{}, step + 1);
   }
 
   // epilogue: D[row][col], col = lane % 32, row = 8 (v / 4) + 4 h + v % 4
   if (!c.n_ok) return;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
+    // rows the fused gather skips are not written: their slots, loaded all
+    // at once before any store
+    uint32_t skip = 0;
+    if (g.slots) {
+      int sl[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = c.p0 + rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
+        sl[v] = g.slots[row < c.r_end ? row : c.p0];
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (sl[v] < 0 || sl[v] >= g.T * g.slot_div) skip |= 1u << v;
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = c.p0 + rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
-      if (row >= c.r_end) continue;
-      if (g.slots) {
-        const int slot = g.slots[row];
-        if (slot < 0 || slot >= g.T * g.slot_div) continue;
-      }
+      if (row >= c.r_end || ((skip >> v) & 1u)) continue;
       g.y[(size_t)row * c.N + c.n] = f32_to_bf16(ldexpf(acc[rt][v], c.sexp));
     }
   }
@@ -294,10 +327,24 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   // per-row power-of-two scale from the row's largest block absmax
   const int n = n_wave + i;
   const bool n_ok = n < N;
+  // (16 independent loads per round: an index past the row re-reads a block
+  // of the same row, which leaves the maximum unchanged)
   float m = 0.0f;
-  if (n_ok) {
-    const float* ar = aexp + (size_t)n * bpr;
-    for (int bk = h; bk < bpr; bk += 2) m = fmaxf(m, ar[bk]);
+  {
+    const float* ar = aexp + (n_ok ? (size_t)n * bpr : 0);
+    float mu[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mu[u] = 0.0f;
+    for (int bk0 = h; bk0 < bpr; bk0 += 32) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int bk = bk0 + 2 * u;
+        mu[u] = fmaxf(mu[u], ar[bk < bpr ? bk : h]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m = fmaxf(m, mu[u]);
+    if (!n_ok) m = 0.0f;
   }
   m = fmaxf(m, __shfl_xor(m, 32, kWave));
   int sexp = 0;
