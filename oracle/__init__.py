@@ -26,6 +26,11 @@ What the oracle computes, and the passage each step follows:
 * ``gemm``  -- the grouped expert GEMM in fp64 over the decoded weights.
   Same README, opening section and "The claim" (fp32 accumulation, bf16
   epilogue, one launch for all active experts).
+* ``moe``   -- the steps on either side of the GEMM: the SwiGLU activation
+  between the two expert projections and the weighted top-k combine after
+  the down projection (landing page "grouped-nf4-gemm", "Owns" and "Use this
+  when": decode glue kernels), and one MoE feed-forward layer composed from
+  all the steps.
 
 Readings where the pages are silent (block size 64 along K, first element in
 the high nibble, ties to the lower code, top-k order and tie-break, stable
@@ -40,10 +45,12 @@ from .nf4 import (NF4_TABLE, ref_pack, ref_unpack, ref_codes, ref_quantize_block
                   ref_byte_ratio_vs_bf16)
 from .route import ref_topk, ref_sort, ref_route_sort
 from .gemm import ref_group_rows, ref_grouped_gemm, ref_grouped_gemm_entries
+from .moe import ref_silu, ref_swiglu, ref_combine, ref_expert_projection, ref_moe_ffn
 
 __all__ = [
     "NF4_TABLE", "ref_pack", "ref_unpack", "ref_codes", "ref_quantize_block",
     "ref_byte_ratio_vs_bf16",
     "ref_topk", "ref_sort", "ref_route_sort",
     "ref_group_rows", "ref_grouped_gemm", "ref_grouped_gemm_entries",
+    "ref_silu", "ref_swiglu", "ref_combine", "ref_expert_projection", "ref_moe_ffn",
 ]

@@ -53,8 +53,13 @@ def ref_sort(topk_ids, num_experts):
     """Stable counting sort of flat slots by expert.
 
     Returns a dict with ``expert_offsets int32[E+1]``, ``sorted_slots
-    int32[M]``, ``group_sizes int32[E]``, ``group_expert_ids int32[E]`` and
-    ``num_groups`` (int), M = T * top_k.
+    int32[M]``, ``slot_rows int32[M]``, ``group_sizes int32[E]``,
+    ``group_expert_ids int32[E]`` and ``num_groups`` (int), M = T * top_k.
+
+    ``slot_rows[s]`` is the grouped row of flat slot s, from its definition:
+    the rows of expert e start at ``expert_offsets[e]`` and a slot comes after
+    every earlier slot (lower s) routed to the same expert.  It is the inverse
+    of ``sorted_slots``; the combine after the down projection reads it.
     """
     ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
     E = int(num_experts)
@@ -63,6 +68,12 @@ def ref_sort(topk_ids, num_experts):
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     sorted_slots = np.argsort(ids, kind="stable")
+    slot_rows = np.empty(ids.size, dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    for slot in range(ids.size):
+        e = ids[slot]
+        slot_rows[slot] = offsets[e] + seen[e]
+        seen[e] += 1
     nonempty = np.nonzero(counts)[0]
     G = nonempty.size
     group_sizes = np.zeros(E, dtype=np.int32)
@@ -72,6 +83,7 @@ def ref_sort(topk_ids, num_experts):
     return {
         "expert_offsets": offsets.astype(np.int32),
         "sorted_slots": sorted_slots.astype(np.int32),
+        "slot_rows": slot_rows.astype(np.int32),
         "group_sizes": group_sizes,
         "group_expert_ids": group_ids,
         "num_groups": int(G),
