@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgnf4.so")
-SOURCES = ["api.hip", "pack.hip", "route.hip", "gather.hip", "decode.hip", "tile.hip"]
+SOURCES = ["api.hip", "pack.hip", "route.hip", "gather.hip", "decode.hip", "tile.hip",
+           "glue.hip"]
 ARCH = "gfx950"
 
 

@@ -97,7 +97,7 @@ size_t gnf4_route_sort_workspace_size(int64_t T, int64_t E, int32_t top_k) {
 
 gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t top_k,
                             int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
-                            int32_t* sorted_slots, int32_t* group_sizes,
+                            int32_t* sorted_slots, int32_t* slot_rows, int32_t* group_sizes,
                             int32_t* group_expert_ids, int32_t* num_groups, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (T < 0 || E <= 0 || top_k < 1 || top_k > E) return GNF4_ERR_INVALID_ARG;
@@ -115,6 +115,10 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
       if (!aligned(p, 4)) return GNF4_ERR_INVALID_ARG;
     for (const void* p : more)
       if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+    if (slot_rows) {  // optional output
+      if (!aligned(slot_rows, 4)) return GNF4_ERR_INVALID_ARG;
+      if (!is_device_ptr(slot_rows)) return GNF4_ERR_NOT_DEVICE_PTR;
+    }
   }
   for (const void* p : dev_ptrs)
     if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
@@ -125,7 +129,7 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
     if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
   }
   const hipError_t e = launch_route_sort(logits, (int)T, (int)E, top_k, topk_ids, topk_w,
-                                         expert_offsets, sorted_slots, group_sizes,
+                                         expert_offsets, sorted_slots, slot_rows, group_sizes,
                                          group_expert_ids, num_groups,
                                          static_cast<int32_t*>(workspace), plan,
                                          (hipStream_t)stream);
@@ -227,6 +231,35 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
     return GNF4_ERR_NOT_DEVICE_PTR;
   const hipError_t e = launch_gather(x, sorted_slots, top_k, (int)T, (int)M, (int)K, x_sorted,
                                      (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
+                        void* stream) {
+  if (M < 0 || I <= 0) return GNF4_ERR_INVALID_ARG;
+  if (M == 0) return GNF4_OK;
+  if (M > ((int64_t)1 << 40) / I) return GNF4_ERR_UNSUPPORTED;
+  if (!gate_up || !h || !aligned(gate_up, 2) || !aligned(h, 2)) return GNF4_ERR_INVALID_ARG;
+  if (!is_device_ptr(gate_up) || !is_device_ptr(h)) return GNF4_ERR_NOT_DEVICE_PTR;
+  const hipError_t e = launch_swiglu(gate_up, M, I, h, (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const float* topk_w,
+                         int64_t T, int32_t top_k, int64_t M, int64_t H, uint16_t* out,
+                         void* stream) {
+  if (T < 0 || M < 0 || H <= 0 || top_k < 1) return GNF4_ERR_INVALID_ARG;
+  if (T == 0) return GNF4_OK;
+  if (T > (int64_t)INT_MAX / top_k) return GNF4_ERR_UNSUPPORTED;
+  if (!slot_rows || !topk_w || !out || (M > 0 && !y)) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(slot_rows, 4) || !aligned(topk_w, 4) || !aligned(out, 2) ||
+      (y && !aligned(y, 2)))
+    return GNF4_ERR_INVALID_ARG;
+  if (!is_device_ptr(slot_rows) || !is_device_ptr(topk_w) || !is_device_ptr(out) ||
+      (M > 0 && !is_device_ptr(y)))
+    return GNF4_ERR_NOT_DEVICE_PTR;
+  const hipError_t e = launch_combine(y, slot_rows, topk_w, T, top_k, M, H, out,
+                                      (hipStream_t)stream);
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 

@@ -168,7 +168,7 @@ RoutePlan plan_route(int64_t T, int64_t E, int top_k);
 
 hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32_t* topk_ids,
                              float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
-                             int32_t* group_sizes, int32_t* group_expert_ids,
+                             int32_t* slot_rows, int32_t* group_sizes, int32_t* group_expert_ids,
                              int32_t* num_groups, int32_t* ws, const RoutePlan& plan,
                              hipStream_t stream);
 
@@ -208,6 +208,12 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t stream);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int T, int M, int K,
                          uint16_t* out, hipStream_t stream);
+
+hipError_t launch_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
+                         hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot_rows, const float* topk_w,
+                          int64_t T, int top_k, int64_t M, int64_t H, uint16_t* out,
+                          hipStream_t stream);
 
 int device_cu_count();
 

@@ -46,6 +46,7 @@ struct RouteArgs {
   float* topk_w;
   int32_t* offsets;
   int32_t* sorted;
+  int32_t* rows;     // optional: grouped row of each flat slot
   int32_t* gsizes;
   int32_t* gids;
   int32_t* ngroups;
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(kWave) void route_one_token_kernel(RouteArgs a) {
       a.topk_ids[rank[s]] = e;
       a.topk_w[rank[s]] = ex[s] / sum;
       a.sorted[pos] = rank[s];  // slot t * k + j with t = 0
+      if (a.rows) a.rows[rank[s]] = pos;
       a.gsizes[pos] = 1;
       a.gids[pos] = e;
     }
@@ -225,7 +227,8 @@ __device__ void scan_and_groups(const int32_t* cnt, int32_t* base, const RouteAr
 // One wave: stable scatter of slots [s0, s1) whose experts are ids[s - s0],
 // starting from per-expert bases in LDS (updated in place).
 __device__ void scatter_slots(const int32_t* ids, int s0, int s1, int32_t* base, int E,
-                              int32_t* __restrict__ sorted, int lane) {
+                              int32_t* __restrict__ sorted, int32_t* __restrict__ rows,
+                              int lane) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
@@ -245,6 +248,7 @@ __device__ void scatter_slots(const int32_t* ids, int s0, int s1, int32_t* base,
     __builtin_amdgcn_wave_barrier();  // every lane reads base[e] before any update
     if (active) {
       sorted[start + rank] = s;
+      if (rows) rows[s] = start + rank;
       const bool leader = (peers & lt) == 0;
       if (leader) base[e] = start + __popcll(peers);
     }
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a)
   if (wave == 0) {
     scan_and_groups(s_cnt, s_base, a, lane);
     __builtin_amdgcn_wave_barrier();
-    scatter_slots(s_ids, 0, M, s_base, a.E, a.sorted, lane);
+    scatter_slots(s_ids, 0, M, s_base, a.E, a.sorted, a.rows, lane);
   }
 }
 
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kWave) void route_scatter_kernel(RouteArgs a) {
   const int s1 = min(s0 + kChunkTokens * a.K, a.T * a.K);
   for (int s = s0 + lane; s < s1; s += kWave) s_ids[s - s0] = a.topk_ids[s];
   __builtin_amdgcn_wave_barrier();
-  scatter_slots(s_ids, s0, s1, s_base, a.E, a.sorted, lane);
+  scatter_slots(s_ids, s0, s1, s_base, a.E, a.sorted, a.rows, lane);
 }
 
 // T == 0: zero offsets and groups.
@@ -369,7 +373,7 @@ RoutePlan plan_route(int64_t T, int64_t E, int top_k) {
 
 hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32_t* topk_ids,
                              float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
-                             int32_t* group_sizes, int32_t* group_expert_ids,
+                             int32_t* slot_rows, int32_t* group_sizes, int32_t* group_expert_ids,
                              int32_t* num_groups, int32_t* ws, const RoutePlan& plan,
                              hipStream_t stream) {
   RouteArgs a;
@@ -381,6 +385,7 @@ hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32
   a.topk_w = topk_w;
   a.offsets = expert_offsets;
   a.sorted = sorted_slots;
+  a.rows = slot_rows;
   a.gsizes = group_sizes;
   a.gids = group_expert_ids;
   a.ngroups = num_groups;

@@ -58,7 +58,12 @@ def library():
     lib.gnf4_route_sort_workspace_size.restype = sz
     lib.gnf4_route_sort_workspace_size.argtypes = [i64, i64, i32]
     lib.gnf4_route_sort.restype = ctypes.c_int
-    lib.gnf4_route_sort.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gnf4_route_sort.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    vp]
+    lib.gnf4_swiglu.restype = ctypes.c_int
+    lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
+    lib.gnf4_combine.restype = ctypes.c_int
+    lib.gnf4_combine.argtypes = [vp, vp, vp, i64, i32, i64, i64, vp, vp]
     lib.gnf4_gather_rows.restype = ctypes.c_int
     lib.gnf4_gather_rows.argtypes = [vp, i64, i64, vp, i32, i64, vp, vp]
     lib.gnf4_grouped_gemm_workspace_size.restype = sz
@@ -135,6 +140,7 @@ class RouteResult:
     topk_w: torch.Tensor          # fp32 [T, k]
     expert_offsets: torch.Tensor  # int32 [E + 1]
     sorted_slots: torch.Tensor    # int32 [T * k]
+    slot_rows: torch.Tensor       # int32 [T * k]: grouped row of each flat slot
     group_sizes: torch.Tensor     # int32 [E]
     group_expert_ids: torch.Tensor  # int32 [E]
     num_groups: torch.Tensor      # int32 [1]
@@ -151,6 +157,7 @@ class RouteBuffers:
             topk_w=torch.empty((T, top_k), dtype=torch.float32, device=device),
             expert_offsets=torch.empty(E + 1, **i32),
             sorted_slots=torch.empty(T * top_k, **i32),
+            slot_rows=torch.empty(T * top_k, **i32),
             group_sizes=torch.empty(E, **i32),
             group_expert_ids=torch.empty(E, **i32),
             num_groups=torch.empty(1, **i32),
@@ -169,10 +176,43 @@ def route_sort(logits, top_k, buffers=None):
     r = buffers.result
     _check(library().gnf4_route_sort(
         _ptr(logits), T, E, top_k, _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.expert_offsets),
-        _ptr(r.sorted_slots), _ptr(r.group_sizes), _ptr(r.group_expert_ids),
+        _ptr(r.sorted_slots), _ptr(r.slot_rows), _ptr(r.group_sizes), _ptr(r.group_expert_ids),
         _ptr(r.num_groups), _ptr(buffers.workspace), buffers.ws_bytes, _stream()),
         "gnf4_route_sort")
     return r
+
+
+# ------------------------------------------------------------ swiglu / combine
+
+def swiglu(gate_up, out=None):
+    """h = silu(gate) * up for ``gate_up`` [M, 2I] bf16 (gate half first) -> [M, I]."""
+    _need(gate_up, "gate_up", torch.bfloat16, 2)
+    M, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up width must be even ([gate | up])")
+    I = two_i // 2
+    if out is None:
+        out = torch.empty((M, I), dtype=torch.bfloat16, device=gate_up.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _check(library().gnf4_swiglu(_ptr(gate_up), M, I, _ptr(out), _stream()), "gnf4_swiglu")
+    return out
+
+
+def combine(y, slot_rows, topk_w, out=None):
+    """out[t] = sum_j topk_w[t, j] * y[slot_rows[t*k + j]] (bf16 [T, H])."""
+    _need(y, "y", torch.bfloat16, 2)
+    _need(slot_rows, "slot_rows", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    T, k = topk_w.shape
+    M, H = y.shape
+    if slot_rows.numel() != T * k:
+        raise ValueError("slot_rows must hold T * k entries")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _check(library().gnf4_combine(_ptr(y) if M > 0 else ctypes.c_void_p(0), _ptr(slot_rows),
+                                  _ptr(topk_w), T, k, M, H, _ptr(out), _stream()), "gnf4_combine")
+    return out
 
 
 # ------------------------------------------------------------ gather_rows

@@ -111,6 +111,9 @@ gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int6
  *                     by ascending expert id, ascending s inside an expert
  *                     (stable; row r of the grouped activations is token
  *                     sorted_slots[r] / top_k)
+ *   slot_rows         [T * top_k] int32 out, optional (NULL: not written): the
+ *                     grouped row of each flat slot, slot_rows[sorted_slots[r]]
+ *                     == r; gnf4_combine reads it
  *   group_sizes       [E] int32 out: rows of each non-empty expert, in
  *                     ascending expert id; the tail after num_groups is zero
  *   group_expert_ids  [E] int32 out: the matching expert ids; tail zero
@@ -127,7 +130,7 @@ size_t gnf4_route_sort_workspace_size(int64_t T, int64_t E, int32_t top_k);
 
 gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t top_k,
                             int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
-                            int32_t* sorted_slots, int32_t* group_sizes,
+                            int32_t* sorted_slots, int32_t* slot_rows, int32_t* group_sizes,
                             int32_t* group_expert_ids, int32_t* num_groups,
                             void* workspace, size_t workspace_bytes, void* stream);
 
@@ -148,6 +151,55 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
  */
 gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int32_t* sorted_slots,
                              int32_t top_k, int64_t M, uint16_t* x_sorted, void* stream);
+
+/*
+ * gnf4_swiglu -- the activation between the two expert projections:
+ * h[r, i] = silu(gate_up[r, i]) * gate_up[r, I + i] for r < M, i < I, with
+ * silu(g) = g / (1 + exp(-g)).
+ *
+ * Landing page "grouped-nf4-gemm", "Owns" (swiglu among the decode glue
+ * kernels) and "Use this when" (the activation as one launch of the decode
+ * step).  The pages do not fix the layout: the gate half comes first.
+ *
+ *   gate_up  [M, 2I] bf16 bits (the gate_up GEMM's output: gate, then up)
+ *   h        [M, I] bf16 bits out
+ *
+ * Computed in fp32 from the bf16 inputs and rounded once to bf16 (round to
+ * nearest even); |h - exact| <= 2^-8 |exact| per element for finite inputs.
+ * 16-byte aligned rows with I % 8 == 0 take a vectorised path; any other
+ * shape or alignment is also accepted.  Errors: GNF4_ERR_INVALID_ARG (null
+ * pointer, M < 0, I <= 0, odd address), GNF4_ERR_UNSUPPORTED (M * I >= 2^40),
+ * GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_HIP.
+ */
+gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
+                        void* stream);
+
+/*
+ * gnf4_combine -- the weighted top-k combine after the down projection:
+ * out[t, :] = sum_{j < top_k} topk_w[t, j] * y[slot_rows[t * top_k + j], :].
+ *
+ * Landing page "grouped-nf4-gemm", "Owns" (combine among the decode glue
+ * kernels) and "Use this when" (the top-k combine as one launch); page
+ * "grouped-nf4-gemm -- single-launch W4A16 GEMM ...": routing weights are not
+ * applied inside the expert GEMM, so they are applied here.
+ *
+ *   y          [M, H] bf16 bits: expert outputs in grouped (sorted) row order
+ *              (may be NULL when M == 0)
+ *   slot_rows  [T * top_k] int32: grouped row of each flat slot, as
+ *              gnf4_route_sort writes it
+ *   topk_w     [T, top_k] fp32 routing weights
+ *   out        [T, H] bf16 bits out; every row is written
+ *
+ * The k terms of a token are accumulated in fp32 in ascending j (fixed
+ * order, deterministic) and rounded once to bf16.  A slot whose row lies
+ * outside [0, M) contributes nothing (a token with no rows gets zeros).
+ * Errors: GNF4_ERR_INVALID_ARG (null pointer, T < 0, M < 0, H <= 0,
+ * top_k < 1, misalignment), GNF4_ERR_UNSUPPORTED (T * top_k >= 2^31),
+ * GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_HIP.
+ */
+gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const float* topk_w,
+                         int64_t T, int32_t top_k, int64_t M, int64_t H, uint16_t* out,
+                         void* stream);
 
 /*
  * gnf4_grouped_gemm -- y = x_sorted . dequant(W[expert_ids[g]])^T per group,

@@ -24,7 +24,7 @@ def _run_and_compare(logits, k, what):
     assert np.array_equal(ids, ref["topk_ids"]), f"{what}: topk ids differ"
     w = r.topk_w.cpu().numpy()
     assert np.max(np.abs(w - ref["topk_w"]), initial=0.0) <= 1e-6, f"{what}: weights"
-    for key in ("expert_offsets", "sorted_slots", "group_sizes", "group_expert_ids"):
+    for key in ("expert_offsets", "sorted_slots", "slot_rows", "group_sizes", "group_expert_ids"):
         got = getattr(r, key).cpu().numpy()
         assert np.array_equal(got, ref[key]), f"{what}: {key} differs"
     assert int(r.num_groups.cpu()[0]) == ref["num_groups"], f"{what}: num_groups"

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("gnf4_pack", "gnf4_route_sort", "gnf4_grouped_gemm", "gnf4_gather_rows"):
+    for required in ("gnf4_pack", "gnf4_route_sort", "gnf4_grouped_gemm", "gnf4_gather_rows",
+                     "gnf4_grouped_gemm_gather", "gnf4_swiglu", "gnf4_combine"):
         assert required in names
 
 
@@ -75,7 +76,7 @@ def test_pack_rejects_bad_arguments(lib):
 
 
 def test_route_rejects_bad_arguments(lib):
-    args = [FAKE] * 7 + [NULL, 0, NULL]
+    args = [FAKE] * 8 + [NULL, 0, NULL]
     assert lib.gnf4_route_sort(FAKE, 4, 8, 0, *args) == 1        # top_k < 1
     assert lib.gnf4_route_sort(FAKE, 4, 8, 9, *args) == 1        # top_k > E
     assert lib.gnf4_route_sort(FAKE, 4, 2048, 8, *args) == 3     # E > 1024
@@ -103,6 +104,27 @@ def test_gemm_rejects_bad_arguments(lib):
     assert call(G=0) == 0
     assert call(x=ctypes.c_void_p(0x1004)) == 1   # x must be 16-byte aligned
     assert lib.gnf4_gather_rows(FAKE, 4, 96, FAKE, 2, 8, FAKE, NULL) == 1
+
+
+def test_glue_argument_errors(lib):
+    # swiglu(gate_up, M, I, h, stream)
+    assert lib.gnf4_swiglu(FAKE, 0, 8, FAKE, NULL) == 0        # M == 0: nothing to do
+    assert lib.gnf4_swiglu(FAKE, -1, 8, FAKE, NULL) == 1
+    assert lib.gnf4_swiglu(FAKE, 4, 0, FAKE, NULL) == 1
+    assert lib.gnf4_swiglu(NULL, 4, 8, FAKE, NULL) == 1
+    assert lib.gnf4_swiglu(FAKE, 4, 8, NULL, NULL) == 1
+    assert lib.gnf4_swiglu(ctypes.c_void_p(0x1001), 4, 8, FAKE, NULL) == 1   # odd address
+    assert lib.gnf4_swiglu(FAKE, 1 << 30, 1 << 20, FAKE, NULL) == 3          # M * I >= 2^40
+    # combine(y, slot_rows, topk_w, T, k, M, H, out, stream)
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, 0, 8, 8, 64, FAKE, NULL) == 0  # T == 0
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, -1, 8, 8, 64, FAKE, NULL) == 1
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, 1, 0, 8, 64, FAKE, NULL) == 1  # top_k < 1
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, 1, 8, -1, 64, FAKE, NULL) == 1
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, 1, 8, 8, 0, FAKE, NULL) == 1   # H <= 0
+    assert lib.gnf4_combine(FAKE, NULL, FAKE, 1, 8, 8, 64, FAKE, NULL) == 1
+    assert lib.gnf4_combine(NULL, FAKE, FAKE, 1, 8, 8, 64, FAKE, NULL) == 1  # y null, M > 0
+    assert lib.gnf4_combine(FAKE, ctypes.c_void_p(0x1002), FAKE, 1, 8, 8, 64, FAKE, NULL) == 1
+    assert lib.gnf4_combine(FAKE, FAKE, FAKE, 1 << 29, 8, 8, 64, FAKE, NULL) == 3  # T*k >= 2^31
 
 
 def test_no_cpu_fallback_in_binding():
