@@ -41,6 +41,17 @@ def gemm_bytes(n_touched, M, N, K):
     return n_touched * (N * K // 2 + 4 * N * K // 64) + 2 * M * K + 2 * M * N
 
 
+def swiglu_bytes(M, I):
+    """gate_up [M, 2I] read once, h [M, I] written once (bf16)."""
+    return 2 * M * 2 * I + 2 * M * I
+
+
+def combine_bytes(T, k, M, H):
+    """Expert rows [M, H] read once, slot rows and weights read, out [T, H]
+    written once."""
+    return 2 * M * H + 8 * T * k + 2 * T * H
+
+
 def route_bytes(T, E, k):
     M = T * k
     return 4 * T * E + 8 * T * k + 4 * (E + 1) + 4 * M + 8 * E + 4
@@ -54,6 +65,8 @@ def parse():
     ap.add_argument("--workload", default="olmoe")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--cells", default="", help="also time every workload's GEMMs into this JSONL")
+    ap.add_argument("--glue", default="",
+                    help="time the SwiGLU and top-k combine kernels alone into this JSONL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -250,6 +263,64 @@ def time_cells(path, dev):
     out.close()
 
 
+def time_glue(path, dev, reps=10):
+    """gnf4_swiglu and gnf4_combine alone at the decode (OLMoE, T=1) and
+    prefill (DSV3, T=4096) shapes of the MoE layer: back-to-back launches
+    from one HIP graph over enough buffer copies that the prefill buffers
+    stream from HBM (the decode buffers are a few tens of KB: those launches
+    are latency, not bandwidth)."""
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    out = open(path, "w")
+    for name in ("olmoe", "dsv3"):
+        wl = wls.WORKLOADS[name]
+        D, N1 = wl.gemm("gate_up")
+        I = N1 // 2
+        r = gnf4.route_sort(torch.from_numpy(wls.router_logits(wl)).to(dev), wl.top_k)
+        M, T, k = wl.M, wl.T, wl.top_k
+        cases = (("swiglu", swiglu_bytes(M, I), (M, 2 * I), (M, I)),
+                 ("combine", combine_bytes(T, k, M, D), (M, D), (T, D)))
+        for kern, byt, in_shape, out_shape in cases:
+            copies = max(2, min(16, -(-(1 << 30) // byt)))
+            gen = torch.Generator(device=dev).manual_seed(5)
+            ins = [torch.randn(in_shape, device=dev, generator=gen).to(torch.bfloat16)
+                   for _ in range(copies)]
+            outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=dev)
+                    for _ in range(copies)]
+            per = 4 * copies
+
+            def launches():
+                for i in range(per):
+                    c = i % copies
+                    if kern == "swiglu":
+                        gnf4.swiglu(ins[c], out=outs[c])
+                    else:
+                        gnf4.combine(ins[c], r.slot_rows, r.topk_w, out=outs[c])
+            graph = capture(launches)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            graph.replay()
+            torch.cuda.synchronize()
+            for i in range(reps):
+                evs[i][0].record()
+                graph.replay()
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            us = sorted(s_.elapsed_time(e_) * 1e3 / per for s_, e_ in evs)
+            med = us[len(us) // 2]
+            rec = {"kernel": kern, "workload": name, "M": M, "T": T, "top_k": k,
+                   "width": I if kern == "swiglu" else D, "bytes": byt,
+                   "median_us": round(med, 3), "GBps": round(byt / med / 1e3, 1),
+                   "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4), "copies": copies}
+            out.write(json.dumps(rec) + "\n")
+            out.flush()
+            print(f"[glue] {json.dumps(rec)}", file=sys.stderr, flush=True)
+            del ins, outs
+            torch.cuda.empty_cache()
+    out.close()
+
+
 KERNEL_SOURCES = ("grouped_nf4_expert_amd/csrc/decode.hip",
                   "grouped_nf4_expert_amd/csrc/gnf4_internal.h")
 
@@ -332,6 +403,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     gnf4.library()
     dev = torch.device("cuda:0")
+
+    if args.glue:
+        time_glue(args.glue, dev)
+        return
 
     if args.copy_mb:
         # calibration for the HBM byte counters: a plain copy of known size
