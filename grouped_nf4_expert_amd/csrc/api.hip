@@ -36,6 +36,11 @@ bool is_device_ptr(const void* p) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Workspace of one grouped GEMM call: the tile path's activation-row
+// exponents (M int32) first, then the decode path's split-K partials, each
+// region 256-byte aligned.
+size_t row_exp_bytes(int64_t M) { return ((size_t)M * sizeof(int32_t) + 255) & ~(size_t)255; }
+
 }  // namespace
 
 int device_cu_count() {
@@ -172,6 +177,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
   a.ids = ids;
   a.y = y;
   a.partial = nullptr;
+  a.row_exp = nullptr;
   a.E = (int)E;
   a.N = (int)N;
   a.K = (int)K;
@@ -193,26 +199,35 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
     if (M <= kDecodeMaxRows) run_tile = false;
   }
   const hipStream_t s = (hipStream_t)stream;
+  size_t dec_off = 0;  // where the decode partials start in the workspace
+  if (ws && (run_tile || ws_bytes > 0)) {
+    if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
+    if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
+  }
+  if (run_tile) {
+    dec_off = row_exp_bytes(M);
+    if (!ws || ws_bytes < dec_off) return GNF4_ERR_WORKSPACE;
+    a.row_exp = static_cast<int32_t*>(ws);
+  }
   if (run_decode) {
     DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
     if (p.L == 0) return GNF4_ERR_UNSUPPORTED;  // this split_k leaves too much K per split
     const size_t need = decode_workspace_bytes(p, M, N);
     if (need > 0) {
-      if (!ws || ws_bytes < need) {
+      if (!ws || ws_bytes < dec_off + need) {
         if (split_k > 0) return GNF4_ERR_WORKSPACE;
         p = plan_decode(M, N, K, G, 1, device_cu_count());  // no room to split: one pass
         if (p.L == 0) return GNF4_ERR_WORKSPACE;  // K needs splitting, which needs workspace
       } else {
-        if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
-        if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
-        a.partial = static_cast<float*>(ws);
+        a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + dec_off);
       }
     }
     const hipError_t e = launch_decode(a, p, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (run_tile) {
-    const hipError_t e = launch_tile(a, s);
+    hipError_t e = launch_row_exp(a, s);
+    if (e == hipSuccess) e = launch_tile(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   return GNF4_OK;
@@ -277,9 +292,12 @@ gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t
 size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
                                            int64_t E, int32_t path, int32_t split_k) {
   (void)E;
-  if (M <= 0 || N <= 0 || K < kBlock || G <= 0 || path == 2) return 0;
+  if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
+  const bool tile = path == 2 || (path == 0 && M > kDecodeMaxRows);
+  const size_t tile_bytes = tile ? row_exp_bytes(M) : 0;
+  if (path == 2) return tile_bytes;
   const DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
-  return decode_workspace_bytes(p, M, N);
+  return tile_bytes + decode_workspace_bytes(p, M, N);
 }
 
 size_t gnf4_grouped_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E) {

@@ -180,6 +180,7 @@ struct GemmArgs {
   const int32_t* ids;
   uint16_t* y;
   float* partial;     // split-K partials [S, M, N] (decode path)
+  int32_t* row_exp;   // per-row power-of-two exponent of the activations [M] (tile path)
   // Optional fused gather: when `slots` is set, output row r uses activation
   // row slots[r] / slot_div of x (x is then [T, K]); a slot outside
   // [0, T * slot_div) leaves row r unwritten.
@@ -205,6 +206,7 @@ size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N);
 
 hipError_t launch_decode(const GemmArgs& a, const DecodePlan& p, hipStream_t stream);
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_row_exp(const GemmArgs& a, hipStream_t stream);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int T, int M, int K,
                          uint16_t* out, hipStream_t stream);

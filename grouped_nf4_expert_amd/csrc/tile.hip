@@ -12,16 +12,19 @@
 // while fp16 weights rounded ONCE from the fp32 product absmax * level are
 // well inside it.  So each weight row n gets a power-of-two scale 2^-s_n that
 // brings its largest block absmax into [0.5, 1); codes are decoded straight
-// to fp16(level * absmax * 2^-s_n) (fp32 product, one rounding), activations
-// are bf16 -> fp16 (exact inside the fp16 range), products accumulate in
-// fp32 on the matrix core, and the epilogue multiplies by 2^s_n exactly and
-// rounds to bf16.
+// to fp16(level * absmax * 2^-s_n) (fp32 product, one rounding).  Each
+// activation row m gets its own power-of-two scale 2^t_m (a pre-pass over the
+// rows, row_exp_kernel) that puts its largest |x| in [2^14, 2^15), so every
+// bf16 value converts to fp16 exactly whatever the row's magnitude (down to
+// 2^-28 of the row maximum, below which values no longer matter), with no
+// overflow.  Products accumulate in fp32 on the matrix core and the epilogue
+// multiplies by 2^(s_n - t_m) exactly before rounding to bf16.
 //
 // Work layout (XCD-aware): a workgroup of 8 wavefronts owns one (group, 256
 // output columns) tile and walks K in steps of 128 (two absmax blocks).  All
 // workgroups of one group's column tiles are dispatched to the same XCD so
 // the group's activation rows stay in that XCD's L2.  Each wavefront owns 32
-// columns (one MFMA column tile) for every row of the group (up to 6 row
+// columns (one MFMA column tile) for every row of the group (up to 5 row
 // tiles of 32 per pass), so every code is decoded exactly once per pass; one
 // column tile per wavefront keeps the registers within two wavefronts per
 // SIMD, so one wavefront's decode overlaps the other's matrix-core work:
@@ -50,12 +53,14 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 512;      // 8 wavefronts, two per SIMD
 constexpr int kTileN = 256;        // output columns per workgroup (32 per wavefront)
 constexpr int kStepK = 128;        // K per main-loop step
-constexpr int kRowTiles = 6;       // 32-row MFMA tiles per pass
+constexpr int kRowTiles = 5;       // 32-row MFMA tiles per pass
 constexpr int kPassRows = 32 * kRowTiles;
+static_assert(kPassRows <= 512, "one exponent per thread and pass");
 constexpr int kLdsRow = kStepK + 8;  // fp16 elements per staged row (padded)
 
 struct TileKArgs {
   GemmArgs g;
+  bool exp_by_token;  // row_exp holds one exponent per token row of x (fused gather)
   int n_tiles;
   int n_work;   // group slots * n_tiles
 };
@@ -115,16 +120,22 @@ __device__ __forceinline__ half8 decode8(uint32_t d, const Table& t) {
   return r;
 }
 
-// 8 bf16 (natural K order) -> 8 fp16 in the decode's slot order.  bf16 values
-// inside the fp16 range convert exactly, so round-toward-zero packing is
-// exact there (and clamps instead of overflowing outside it).
-__device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
+// 8 bf16 (natural K order), times 2^t when SCALED, -> 8 fp16 in the
+// decode's slot order.  The row's exponent keeps every value below 2^15, and
+// bf16 values in the fp16 normal range convert exactly, so round-toward-zero
+// packing is exact.
+template <bool SCALED>
+__device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v, int t) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
   float f[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     f[2 * j] = __uint_as_float(d[j] << 16);
     f[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+    if constexpr (SCALED) {
+      f[2 * j] = ldexpf(f[2 * j], t);
+      f[2 * j + 1] = ldexpf(f[2 * j + 1], t);
+    }
   }
   uint4 r;
   r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[2]));
@@ -138,6 +149,7 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
 struct PassCtx {
   const TileKArgs* a;
   _Float16* s_x;           // [2][kPassRows * kLdsRow]
+  int* s_exp;              // [kPassRows] activation exponents of the pass's rows
   const uint8_t* wrow;     // this lane's weight row (or row 0 when out of range)
   const float* arow;       // its absmax row
   bool n_ok;               // the lane's column exists
@@ -161,7 +173,7 @@ __device__ __forceinline__ int div_slot(int n, int d) {
 // dropped where the values are used: zero activations at staging, a zero
 // decode table for an absent weight block.
 template <int RT>
-__device__ __forceinline__ void tile_pass(const PassCtx& c) {
+__device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
   const GemmArgs& g = c.a->g;
   constexpr int kChunks = RT;  // 16-byte x chunks per thread: RT*32 rows x 16 chunks / 512 threads
   float16v acc[RT];
@@ -186,6 +198,8 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
     }
     xsrc[j] = src;
   }
+  // the pass's activation scale exponents, in LDS for staging and epilogue
+
   // Two register sets (activations and weights) alternate between steps so
   // every load is issued two steps before it is used: step s computes from
   // LDS buffer s % 2, then stages step s + 1's activations (loaded during
@@ -213,8 +227,9 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
       const int q = c.tid + kThreads * j;
       const int row = q >> 4, c16 = q & 15;
       const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
+      const uint4 v = ok ? xr[sl][j] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&c.s_x[buf * (kPassRows * kLdsRow) + row * kLdsRow + 8 * c16]) =
-          bf16x8_to_f16_slots(ok ? xr[sl][j] : make_uint4(0, 0, 0, 0));
+          scaled ? bf16x8_to_f16_slots<true>(v, c.s_exp[row]) : bf16x8_to_f16_slots<false>(v, 0);
     }
   };
   // weight codes: the lane's 32 bytes of block h of the step, and its absmax
@@ -291,13 +306,14 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
     for (int v = 0; v < 16; ++v) {
       const int row = c.p0 + rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
       if (row >= c.r_end || ((skip >> v) & 1u)) continue;
-      g.y[(size_t)row * c.N + c.n] = f32_to_bf16(ldexpf(acc[rt][v], c.sexp));
+      g.y[(size_t)row * c.N + c.n] = f32_to_bf16(ldexpf(acc[rt][v], c.sexp - c.s_exp[row - c.p0]));
     }
   }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
+  __shared__ int s_exp[kPassRows];
 
   // XCD-aware order: consecutive work items land on one XCD.
   const int nb = gridDim.x;
@@ -323,6 +339,17 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
   const float* aexp = a.g.absmax + (size_t)e * N * bpr;
+
+  // activation exponent of output row `row` (by token when the gather is
+  // fused and the exponents were taken per token); the first pass's are
+  // loaded now, so their latency overlaps the absmax loads below
+  auto row_exp_of = [&](int row) -> int {
+    if (!a.exp_by_token) return a.g.row_exp[row];
+    const int slot = a.g.slots[row];
+    return (slot >= 0 && slot < a.g.T * a.g.slot_div) ? a.g.row_exp[div_slot(slot, a.g.slot_div)]
+                                                       : 0;
+  };
+  const int t_first = tid < min(kPassRows, r_end - r_begin) ? row_exp_of(r_begin + tid) : 0;
 
   // per-row power-of-two scale from the row's largest block absmax
   const int n = n_wave + i;
@@ -353,6 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   PassCtx c;
   c.a = &a;
   c.s_x = &s_x[0][0];
+  c.s_exp = s_exp;
   c.wrow = wexp + (n_ok ? (size_t)n * row_bytes : 0);
   c.arow = aexp + (n_ok ? (size_t)n * bpr : 0);
   c.n_ok = n_ok;
@@ -370,23 +398,96 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   for (int p0 = r_begin; p0 < r_end; p0 += kPassRows) {
     c.p0 = p0;
     c.rows = min(kPassRows, r_end - p0);
+    // the pass's activation exponents (prefetched for the first pass); rows
+    // of ordinary magnitude have exponent 0, and a pass scales only when one
+    // of its rows needs it
+    int t = 0;
+    if (tid < c.rows) {
+      t = p0 == r_begin ? t_first : row_exp_of(p0 + tid);
+      s_exp[tid] = t;
+    }
+    const bool scaled = __syncthreads_or(t) != 0;
     switch ((c.rows + 31) / 32) {
-      case 1: tile_pass<1>(c); break;
-      case 2: tile_pass<2>(c); break;
-      case 3: tile_pass<3>(c); break;
-      case 4: tile_pass<4>(c); break;
-      case 5: tile_pass<5>(c); break;
-      default: tile_pass<6>(c); break;
+      case 1: tile_pass<1>(c, scaled); break;
+      case 2: tile_pass<2>(c, scaled); break;
+      case 3: tile_pass<3>(c, scaled); break;
+      case 4: tile_pass<4>(c, scaled); break;
+      default: tile_pass<5>(c, scaled); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
 }
 
+// Activation scale exponents, one wavefront per row: per token row of x
+// when `by_token` (fused gather), else per output row r < M with its source
+// (x row r, or its token through the fused gather's slot).  From the
+// largest |x| from the bf16 bit patterns (magnitude order is integer order)
+// and e, the biased exponent of that maximum.  A row whose maximum lies in
+// [2^-6, 2^15) converts to fp16 as it is (t = 0: values down to 2^-14 are
+// exact and smaller ones carry at most 2^-24 absolute error, far inside the
+// tolerance next to such a row's size); any other row gets t = 141 - e, so
+// that max * 2^t lies in [2^14, 2^15).  A row of zeros (or a skipped slot)
+// gets t = 0.
+constexpr int kExpThreads = 256;
+
+__global__ __launch_bounds__(kExpThreads) void row_exp_kernel(GemmArgs g, bool by_token) {
+  const int lane = threadIdx.x % kWave;
+  const int waves = gridDim.x * (kExpThreads / kWave);
+  const int chunks = g.K / 8;
+  const int n_rows = by_token ? g.T : g.M;
+  for (int r = blockIdx.x * (kExpThreads / kWave) + threadIdx.x / kWave; r < n_rows; r += waves) {
+    int src = r;
+    if (g.slots && !by_token) {
+      const int slot = g.slots[r];
+      src = (slot >= 0 && slot < g.T * g.slot_div) ? slot / g.slot_div : -1;
+    }
+    uint32_t mb = 0;
+    if (src >= 0) {
+      const uint4* row = reinterpret_cast<const uint4*>(g.x + (size_t)src * g.K);
+      for (int c0 = lane; c0 < chunks; c0 += 4 * kWave) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int cc = c0 + u * kWave;
+          v[u] = row[cc < chunks ? cc : lane % chunks];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mb = max(mb, max(d[q] & 0x7fffu, (d[q] >> 16) & 0x7fffu));
+        }
+      }
+    }
+    mb = wave_max_u32(mb);
+    const int e = (int)(mb >> 7);
+    if (lane == 0) g.row_exp[r] = (mb == 0 || (e >= 121 && e <= 141)) ? 0 : 141 - e;
+  }
+}
+
 }  // namespace
+
+// With the gather fused, token rows repeat top_k times among the M rows: the
+// exponents are then taken once per token (T <= M entries fit the buffer).
+static bool exp_by_token(const GemmArgs& g) { return g.slots != nullptr && g.T <= g.M; }
+
+hipError_t launch_row_exp(const GemmArgs& g, hipStream_t stream) {
+  const bool by_token = exp_by_token(g);
+  const int n_rows = by_token ? g.T : g.M;
+  if (n_rows <= 0) return hipSuccess;
+  const int per_block = kExpThreads / kWave;
+  const int cap = device_cu_count() * 8;
+  int blocks = (n_rows + per_block - 1) / per_block;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(row_exp_kernel, dim3(blocks), dim3(kExpThreads), 0, stream, g, by_token);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   TileKArgs a;
   a.g = g;
+  a.exp_by_token = exp_by_token(g);
   a.n_tiles = (g.N + kTileN - 1) / kTileN;
   a.n_work = (int)group_slots(g.G, g.M, g.rows_min_tile) * a.n_tiles;
   const int grid = ((a.n_work + 7) / 8) * 8;

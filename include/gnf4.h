@@ -217,27 +217,32 @@ gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const floa
  *   group_expert_ids  [G] int32: expert of group g (duplicates allowed)
  *   y                 [M, N] bf16 bits out; only rows covered by a valid group
  *                     are written, the rest keep their contents
- *   workspace         device scratch of gnf4_grouped_gemm_workspace_size() bytes
+ *   workspace         device scratch of gnf4_grouped_gemm_workspace_size() bytes,
+ *                     16-byte aligned: the tile path's per-row activation
+ *                     exponents (4 M bytes, rounded up to 256) and, when the
+ *                     decode path splits K, its fp32 partials
  *
  * Group g covers rows [sum_{g'<g} max(size_g', 0), + size_g) clipped to M.
  * Routing weights are not applied here (the top-k combine is separate glue).
  * Two kernels implement the same arithmetic contract: a bandwidth-bound
  * decode path for groups with few rows (fp32 decode and multiply-add, optional
  * split-K with a fixed-order fp32 reduce) and a matrix-core tile path for
- * groups with many rows (per-row power-of-two scaling, codes decoded with
- * their block absmax into fp16, fp16 x fp16 -> fp32 MFMA).  Which one runs
- * is a performance choice made from host-known sizes only; both meet
- * |y - exact| <= 8e-3 |exact| + 1e-3 rms(exact) per element for activations
- * within the fp16 range (|x| <= 65504) on the tile path.  Results are
+ * groups with many rows (a power-of-two scale per weight row and per
+ * activation row, codes decoded with their block absmax into fp16, fp16 x
+ * fp16 -> fp32 MFMA).  Which one runs is a performance choice made from
+ * host-known sizes only; both meet |y - exact| <= 8e-3 |exact| +
+ * 1e-3 rms(exact) per element for any finite bf16 activations.  Results are
  * deterministic run to run.
  *
  * Limits: M >= 0, G >= 0 (either 0: nothing to do), E, N >= 1, K >= 64 with
  * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call,
  * G < 65536.  The decode path keeps one K split of an activation row in LDS,
  * at most 319 chunks of 32 (K <= 10208 unsplit); a larger K is split across
- * workgroups, which needs the workspace.
+ * workgroups, which needs the workspace.  Whenever the tile path may run
+ * (M > 8, or path 2 of the _ex form) the workspace is required.
  * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE
- * (also: K too large to run unsplit and no workspace given),
+ * (workspace missing or smaller than the size query returns; also: K too
+ * large to run unsplit and no workspace given),
  * GNF4_ERR_UNSUPPORTED (a limit above exceeded), GNF4_ERR_HIP.
  */
 size_t gnf4_grouped_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);

@@ -204,6 +204,29 @@ def test_adversarial_absmax(scenario, path):
     check_gemm(y, c["y_ref"], c["written"], f"{scenario} path {path}")
 
 
+@pytest.mark.parametrize("scale", [1e-6, 1e-20, 5e4, 1e30])
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_activation_magnitudes(scale, path):
+    """Activation rows far outside fp16's range, tiny and huge, mixed with
+    ordinary rows and an all-zero row.  The tile path scales each row by its
+    own power of two, so every class of rows meets the bar on its own (the
+    rms of the bound is taken per class)."""
+    E, N, K, M = 3, 96, 512, 48
+    rng = np.random.default_rng(13)
+    f = np.ones((M, 1), np.float32)
+    f[::3] = scale
+    f[7] = 0.0
+    x = wls.bf16_round((rng.standard_normal((M, K)) * f).astype(np.float32))
+    c = _custom(E, N, K, [20, 12, 16], [2, 0, 1], M, seed=13, x=x)
+    note(f"gemm activation magnitude {scale:g} path={path}")
+    y = _run_custom(c, path)
+    scaled = np.zeros(M, bool)
+    scaled[::3] = True
+    for cls, mask in (("scaled", scaled), ("ordinary", ~scaled)):
+        check_gemm(y, c["y_ref"], c["written"] & mask, f"x*{scale:g} {cls} rows, path {path}")
+    assert np.all(host_f64(y)[7] == 0.0)
+
+
 @pytest.mark.parametrize("path", [DEC, TILE])
 def test_deterministic(path):
     c = _custom(8, 512, 1024, [3, 20, 1, 40, 6], [7, 2, 2, 5, 0], 70, seed=11)
