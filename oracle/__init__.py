@@ -25,7 +25,8 @@ What the oracle computes, and the passage each step follows:
   landing page.
 * ``gemm``  -- the grouped expert GEMM in fp64 over the decoded weights.
   Same README, opening section and "The claim" (fp32 accumulation, bf16
-  epilogue, one launch for all active experts).
+  epilogue, one launch for all active experts); and its dgrad (the
+  activation gradient over the same packed stack, landing page "Owns").
 * ``moe``   -- the steps on either side of the GEMM: the SwiGLU activation
   between the two expert projections and the weighted top-k combine after
   the down projection (landing page "grouped-nf4-gemm", "Owns" and "Use this
@@ -44,13 +45,13 @@ byte round trips, exact-rational brute force, closed forms, invariants).
 from .nf4 import (NF4_TABLE, ref_pack, ref_unpack, ref_codes, ref_quantize_block,
                   ref_byte_ratio_vs_bf16)
 from .route import ref_topk, ref_sort, ref_route_sort
-from .gemm import ref_group_rows, ref_grouped_gemm, ref_grouped_gemm_entries
+from .gemm import ref_group_rows, ref_grouped_gemm, ref_grouped_gemm_entries, ref_grouped_dgrad
 from .moe import ref_silu, ref_swiglu, ref_combine, ref_expert_projection, ref_moe_ffn
 
 __all__ = [
     "NF4_TABLE", "ref_pack", "ref_unpack", "ref_codes", "ref_quantize_block",
     "ref_byte_ratio_vs_bf16",
     "ref_topk", "ref_sort", "ref_route_sort",
-    "ref_group_rows", "ref_grouped_gemm", "ref_grouped_gemm_entries",
+    "ref_group_rows", "ref_grouped_gemm", "ref_grouped_gemm_entries", "ref_grouped_dgrad",
     "ref_silu", "ref_swiglu", "ref_combine", "ref_expert_projection", "ref_moe_ffn",
 ]

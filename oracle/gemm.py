@@ -94,3 +94,31 @@ def ref_grouped_gemm_entries(x_sorted, expert_weights, num_experts, N,
             out[i] = float(np.dot(x[rows[i]].astype(np.float64),
                                   w.astype(np.float64)))
     return out
+
+
+def ref_grouped_dgrad(dy_sorted, packed, absmax, group_sizes, group_expert_ids):
+    """Gradient of the grouped GEMM with respect to its activations.
+
+    Landing page "grouped-nf4-gemm", "Owns": the grouped packed GEMM and its
+    dgrad (the backward of ``y = x W^T`` over the same packed stack).  For
+    the rows of group g with expert e: ``dx[r, :] = dy[r, :] @ W[e]`` -- a
+    contraction over N, the transpose of the forward GEMM's access to the
+    K-contiguous stack.  Same group reading as ``ref_grouped_gemm``.
+
+    ``dy_sorted``: fp32 ``[M, N]`` (bf16 values widened exactly).
+    Returns ``(dx fp64[M, K], written bool[M])``; unwritten rows are NaN.
+    """
+    dy = np.asarray(dy_sorted, dtype=np.float32)
+    M, N = dy.shape
+    E, N_w, half_k = packed.shape
+    assert N_w == N
+    K = 2 * half_k
+    dx = np.full((M, K), np.nan, dtype=np.float64)
+    written = np.zeros(M, dtype=bool)
+    cache = {}
+    for g, e, r0, r1 in ref_group_rows(group_sizes, group_expert_ids, E, M):
+        if e not in cache:
+            cache[e] = ref_unpack(packed[e], absmax[e]).astype(np.float64)
+        dx[r0:r1] = dy[r0:r1].astype(np.float64) @ cache[e]
+        written[r0:r1] = True
+    return dx, written

@@ -146,3 +146,63 @@ def test_planted_mistakes_are_caught():
             bad_trans = not np.array_equal(trans.astype(np.float64), ref)
             assert bad_trans
     assert bad_sw > 0 and bad_e > 0
+
+
+# ------------------------------------------------------------------ dgrad
+
+def _dgrad_case(seed, E=4, N=96, K=192, sizes=(3, 0, 5, 2), ids=(1, 3, 1, 0), M=11):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((E, N, K)) * 0.05).astype(np.float32)
+    packed, absmax = oracle.ref_pack(w)
+    dy = rng.standard_normal((M, N)).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    return packed, absmax, list(sizes), list(ids), dy, x
+
+
+def test_dgrad_is_the_adjoint_of_the_gemm():
+    """<dy, x W^T> == <dy W, x> over the written rows (exact math; fp64)."""
+    packed, absmax, sizes, ids, dy, x = _dgrad_case(41)
+    y, wr = oracle.ref_grouped_gemm(x, packed, absmax, sizes, ids)
+    dx, wr2 = oracle.ref_grouped_dgrad(dy, packed, absmax, sizes, ids)
+    assert np.array_equal(wr, wr2)
+    lhs = np.sum(dy[wr].astype(np.float64) * y[wr])
+    rhs = np.sum(dx[wr] * x[wr].astype(np.float64))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+def test_dgrad_one_hot_rows_select_weight_rows():
+    packed, absmax, sizes, ids, _, _ = _dgrad_case(43)
+    M, N = 11, 96
+    dy = np.zeros((M, N), np.float32)
+    picks = [(0, 5), (1, 0), (2, 95), (3, 40), (5, 7), (10, 33)]
+    for r, n in picks:
+        dy[r, n] = 1.0
+    dx, wr = oracle.ref_grouped_dgrad(dy, packed, absmax, sizes, ids)
+    owner = {r: e for _g, e, r0, r1 in oracle.ref_group_rows(sizes, ids, 4, M)
+             for r in range(r0, r1)}
+    for r, n in picks:
+        if r in owner:
+            want = oracle.ref_unpack(packed[owner[r]], absmax[owner[r]])[n]
+            np.testing.assert_array_equal(dx[r], want.astype(np.float64))
+        else:
+            assert not wr[r] and np.all(np.isnan(dx[r]))
+
+
+def test_dgrad_matches_explicit_loops():
+    packed, absmax, sizes, ids, dy, _ = _dgrad_case(47, E=3, N=8, K=64, sizes=(2, 1),
+                                                     ids=(2, 0), M=4)
+    dx, wr = oracle.ref_grouped_dgrad(dy, packed, absmax, sizes, ids)
+    table = oracle.NF4_TABLE
+    codes = oracle.ref_codes(packed)
+    rows_of = {0: 2, 1: 2, 2: 0}
+    for r in range(4):
+        if r not in rows_of:
+            assert not wr[r]
+            continue
+        e = rows_of[r]
+        for k in range(64):
+            acc = 0.0
+            for n in range(8):
+                acc += float(dy[r, n]) * float(np.float32(table[codes[e, n, k]]) *
+                                               absmax[e, n, k // 64])
+            assert abs(dx[r, k] - acc) <= 1e-12 * max(1.0, abs(acc))
