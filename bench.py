@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--workload", default="olmoe")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--cells", default="", help="also time every workload's GEMMs into this JSONL")
+    ap.add_argument("--dgrad", default="",
+                    help="time the grouped dgrad alone at each workload's shapes into this JSONL")
     ap.add_argument("--glue", default="",
                     help="time the SwiGLU and top-k combine kernels alone into this JSONL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -263,6 +265,71 @@ def time_cells(path, dev):
     out.close()
 
 
+def time_dgrad(path, dev):
+    """gnf4_grouped_dgrad alone, cycling over enough weight copies to defeat
+    the Infinity Cache (as the forward cells); per-launch HIP events over a
+    graph of back-to-back launches.  Algorithmic bytes as the forward GEMM
+    (each touched expert's codes and absmax once, dy read, dx written)."""
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    out = open(path, "w")
+    cells = (("olmoe", "gate_up"), ("olmoe", "down"), ("qwen3_t8", "gate_up"),
+             ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"))
+    for name, gemm in cells:
+        wl = wls.WORKLOADS[name]
+        lg = torch.from_numpy(wls.router_logits(wl)).to(dev)
+        r = gnf4.route_sort(lg, wl.top_k)
+        G = min(wl.E, wl.M)
+        ng = int(r.num_groups.cpu()[0])
+        K, N = wl.gemm(gemm)
+        stack_bytes = wl.E * (N * K // 2 + N * K // 16)
+        copies = max(1, min(8, int(np.ceil(600e6 / stack_bytes))))
+        stacks = []
+        for ci in range(copies):
+            p = torch.empty((wl.E, N, K // 2), dtype=torch.uint8, device=dev)
+            a = torch.empty((wl.E, N, K // 64), dtype=torch.float32, device=dev)
+            for e in range(wl.E):
+                gnf4.pack(wls.expert_weights_device(wl, gemm, e, dev, 200 + ci), out=(p[e], a[e]))
+            stacks.append((p, a))
+        dy = wls.activations_device(wl.M, N, dev, wl.seed, 60, N)
+        dx = torch.empty((wl.M, K), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(gnf4.library().gnf4_grouped_dgrad_workspace_size(wl.M, N, K, G, wl.E),
+                             16), dtype=torch.uint8, device=dev)
+        per = 4 * copies if name != "dsv3" else 1
+
+        def launches():
+            for i in range(per):
+                p, a = stacks[i % copies]
+                gnf4.grouped_dgrad(dy, p, a, r.group_sizes, r.group_expert_ids, G=G, dx=dx,
+                                   workspace=ws)
+        graph = capture(launches)
+        reps = 10 if name != "dsv3" else 2
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            evs[i][0].record()
+            graph.replay()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        us = sorted(s_.elapsed_time(e_) * 1e3 / per for s_, e_ in evs)
+        med = us[len(us) // 2]
+        byt = gemm_bytes(ng, wl.M, N, K)
+        flops = 2.0 * wl.M * N * K
+        rec = {"kernel": "dgrad", "workload": name, "gemm": gemm, "M": wl.M, "N": N, "K": K,
+               "touched_experts": ng, "median_us": round(med, 2), "GBps": round(byt / med / 1e3, 1),
+               "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
+               "TFLOPs": round(flops / med / 1e6, 2), "weight_copies": copies}
+        out.write(json.dumps(rec) + "\n")
+        out.flush()
+        print(f"[dgrad] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del stacks
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def time_glue(path, dev, reps=10):
     """gnf4_swiglu and gnf4_combine alone at the decode (OLMoE, T=1) and
     prefill (DSV3, T=4096) shapes of the MoE layer: back-to-back launches
@@ -406,6 +473,9 @@ def main():
 
     if args.glue:
         time_glue(args.glue, dev)
+        return
+    if args.dgrad:
+        time_dgrad(args.dgrad, dev)
         return
 
     if args.copy_mb:

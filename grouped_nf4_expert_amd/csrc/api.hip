@@ -249,6 +249,61 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
+size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G,
+                                         int64_t E) {
+  (void)E;
+  if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
+  return dgrad_workspace_bytes(plan_dgrad(M, N, K, G, device_cu_count()), M, K);
+}
+
+gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const float* absmax,
+                               int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                               const int32_t* group_expert_ids, int64_t G, int64_t M,
+                               uint16_t* dx, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
+    return GNF4_ERR_INVALID_ARG;
+  if (M == 0 || G == 0) return GNF4_OK;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) ||
+      M * N >= ((int64_t)1 << 31) || E * N >= ((int64_t)1 << 31) || G >= 65536)
+    return GNF4_ERR_UNSUPPORTED;
+  if (!dy || !packed || !absmax || !group_sizes || !group_expert_ids || !dx)
+    return GNF4_ERR_INVALID_ARG;
+  if (!aligned(dy, 2) || !aligned(dx, 2) || !aligned(packed, 16) || !aligned(absmax, 4) ||
+      !aligned(group_sizes, 4) || !aligned(group_expert_ids, 4))
+    return GNF4_ERR_INVALID_ARG;
+  const void* ptrs[] = {dy, packed, absmax, group_sizes, group_expert_ids, dx};
+  for (const void* p : ptrs)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  DgradArgs a;
+  a.dy = dy;
+  a.packed = packed;
+  a.absmax = absmax;
+  a.sizes = group_sizes;
+  a.ids = group_expert_ids;
+  a.dx = dx;
+  a.partial = nullptr;
+  a.E = (int)E;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)G;
+  a.M = (int)M;
+  DgradPlan p = plan_dgrad(M, N, K, G, device_cu_count());
+  const size_t need = dgrad_workspace_bytes(p, M, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) {
+      p.S = 1;  // no room for split partials: one split over all of N
+      p.rows_per_split = (int)N;
+    } else {
+      if (!aligned(workspace, 16)) return GNF4_ERR_INVALID_ARG;
+      if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
+      a.partial = static_cast<float*>(workspace);
+    }
+  }
+  const hipError_t e = launch_dgrad(a, p, (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
 gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
                         void* stream) {
   if (M < 0 || I <= 0) return GNF4_ERR_INVALID_ARG;

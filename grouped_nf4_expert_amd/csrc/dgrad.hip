@@ -1,0 +1,237 @@
+// Activation gradient of the grouped NF4 GEMM: dx[r, :] = dy[r, :] . W[e]
+// for the rows r of each group (expert e), over the same packed stack.
+//
+// Landing page "grouped-nf4-gemm", "Owns": the grouped packed GEMM and its
+// dgrad.  The contraction runs over N, across the rows of the K-contiguous
+// [N, K/2] codes, so the access is the transpose of the forward GEMM's:
+//  * a lane owns one 16-byte chunk (32 consecutive k) of the weight rows and
+//    accumulates those 32 outputs in fp32 for up to R rows of dy; its
+//    wavefront walks a slice of the N rows, 8 rows in flight at a time
+//    (16-byte code loads coalesced across the 64 lanes of a row, the block
+//    absmax, and dy[r, n], the same for the whole wavefront);
+//  * each code is decoded through a 16-entry fp32 table in LDS at an 8-byte
+//    stride (conflict-free for any mix of codes) and multiplied-added with
+//    dy[r, n] * absmax, computed once per row and block;
+//  * the 8 wavefronts of a workgroup cover disjoint row slices; their
+//    partial sums meet in LDS and are added in wavefront order;
+//  * when N is split across workgroups to fill the machine, each split
+//    writes fp32 partials that a second kernel sums in split order, so the
+//    result is deterministic run to run.
+// Every weight byte is read once per pass of R rows of dy: the kernel is
+// bound by HBM when groups hold few rows (the decode regime).
+
+#include <limits.h>
+
+#include "gnf4_internal.h"
+
+namespace gnf4 {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kNB = 8;          // weight rows in flight per wavefront
+constexpr int kChunkPitch = 33;  // floats per lane in the reduction buffer (conflict-free)
+
+struct DgradKArgs {
+  const uint16_t* dy;   // [M, N] bf16
+  const uint8_t* packed;
+  const float* absmax;
+  const int32_t* sizes;
+  const int32_t* ids;
+  uint16_t* dx;         // [M, K] bf16
+  float* partial;       // [S, M, K] fp32 when S > 1
+  int E, N, K, G, M, S, rows_per_split;
+};
+
+// (byte B of v) & mask in one VALU instruction (SDWA source byte select).
+template <int B>
+__device__ __forceinline__ uint32_t byte_and(uint32_t v, uint32_t mask) {
+  uint32_t r;
+  asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_%3 src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(v), "s"(mask), "n"(B));
+  return r;
+}
+
+__device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
+  __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
+  __shared__ float s_red[kWaves * kWave * kChunkPitch];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  GroupRef gr;
+  if (!find_group(a.sizes, a.ids, a.G, a.E, a.M, 1, INT_MAX, blockIdx.y, gr)) return;
+  if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
+  const int N = a.N, K = a.K;
+  const int cpr = K / 32;                     // 16-byte chunks per weight row
+  const int c = blockIdx.x * kWave + lane;    // this lane's chunk
+  const bool c_ok = c < cpr;
+  const int cc = c_ok ? c : 0;
+  const int bpr = K / kBlock;
+  const size_t row_bytes = (size_t)K / 2;
+  const uint8_t* wexp = a.packed + (size_t)gr.expert * N * row_bytes;
+  const float* aexp = a.absmax + (size_t)gr.expert * N * bpr;
+  const int s = blockIdx.z;
+  const int n_begin = s * a.rows_per_split;
+  const int n_end = min(n_begin + a.rows_per_split, N);
+  const int r_begin = gr.row;
+  const int r_end = min(r_begin + gr.size, a.M);
+
+  for (int r0 = r_begin; r0 < r_end; r0 += R) {
+    float acc[R][32];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) acc[r][j] = 0.0f;
+    // this wavefront's rows: n_begin + wave + kWaves * i
+    for (int n0 = n_begin + wave; n0 < n_end; n0 += kWaves * kNB) {
+      uint4 wq[kNB];
+      float av[kNB];
+      float dv[kNB][R];
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const int n = n0 + kWaves * b;
+        const bool ok = n < n_end;
+        const int nn = ok ? n : n_begin;
+        wq[b] = *reinterpret_cast<const uint4*>(wexp + (size_t)nn * row_bytes + 16 * (size_t)cc);
+        av[b] = (ok && c_ok) ? aexp[(size_t)nn * bpr + (cc >> 1)] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = min(r0 + r, r_end - 1);
+          dv[b][r] = (r0 + r < r_end) ? bf16_to_f32(a.dy[(size_t)row * N + nn]) : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        float sc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r] = dv[b][r] * av[b];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t d = w == 0 ? wq[b].x : w == 1 ? wq[b].y : w == 2 ? wq[b].z : wq[b].w;
+          // LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
+          // byte q hold its high code; after a left shift by 3, its low code
+          const uint32_t dh = d >> 1, dl = d << 3;
+          const uint32_t oh[4] = {byte_and<0>(dh, 0x78u), byte_and<1>(dh, 0x78u),
+                                  byte_and<2>(dh, 0x78u), byte_and<3>(dh, 0x78u)};
+          const uint32_t ol[4] = {byte_and<0>(dl, 0x78u), byte_and<1>(dl, 0x78u),
+                                  byte_and<2>(dl, 0x78u), byte_and<3>(dl, 0x78u)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float vh = lut_at(s_lut, oh[q]);
+            const float vl = lut_at(s_lut, ol[q]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              acc[r][8 * w + 2 * q] = fmaf(sc[r], vh, acc[r][8 * w + 2 * q]);
+              acc[r][8 * w + 2 * q + 1] = fmaf(sc[r], vl, acc[r][8 * w + 2 * q + 1]);
+            }
+          }
+        }
+      }
+    }
+    // wavefront partials meet in LDS; thread t sums outputs t, t + 512, ...
+    // over the wavefronts in order
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      __syncthreads();  // the previous row's readers are done
+      float* mine = s_red + (wave * kWave + lane) * kChunkPitch;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) mine[j] = acc[r][j];
+      __syncthreads();
+      const int row = r0 + r;
+      if (row >= r_end) continue;
+#pragma unroll
+      for (int q = 0; q < (kWave * 32) / kThreads; ++q) {
+        const int p = threadIdx.x + kThreads * q;  // position in the tile: lane p / 32, k p % 32
+        const int pl = p >> 5, pj = p & 31;
+        const int k = 32 * (blockIdx.x * kWave + pl) + pj;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += s_red[(w * kWave + pl) * kChunkPitch + pj];
+        if (k >= K) continue;
+        if (a.S == 1)
+          a.dx[(size_t)row * K + k] = f32_to_bf16(sum);
+        else
+          a.partial[((size_t)s * a.M + row) * K + k] = sum;
+      }
+    }
+  }
+}
+
+// Sum the S split partials of every row a group covers, in split order -> bf16.
+__global__ __launch_bounds__(256) void dgrad_reduce_kernel(DgradKArgs a) {
+  GroupRef gr;
+  if (!find_group(a.sizes, a.ids, a.G, a.E, a.M, 1, INT_MAX, blockIdx.y, gr)) return;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= a.K) return;
+  const int r_end = min(gr.row + gr.size, a.M);
+  const size_t plane = (size_t)a.M * a.K;
+  for (int r = gr.row; r < r_end; ++r) {
+    const float* p = a.partial + (size_t)r * a.K + k;
+    float sum = 0.0f;
+    for (int si = 0; si < a.S; ++si) sum += p[si * plane];
+    a.dx[(size_t)r * a.K + k] = f32_to_bf16(sum);
+  }
+}
+
+}  // namespace
+
+// Launch rule (host-known sizes only): R from the rows per group; N split so
+// the grid holds about two wavefronts per SIMD, each split at least one
+// batch of rows per wavefront.
+DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
+  DgradPlan p;
+  const int64_t g_eff = G < M ? G : M;
+  const double rows_per_group = (double)M / (double)(g_eff > 0 ? g_eff : 1);
+  p.R = rows_per_group <= 1.5 ? 1 : (rows_per_group <= 3.0 ? 2 : 4);
+  p.k_tiles = (int)((K / 32 + kWave - 1) / kWave);
+  const int64_t target_waves = 8LL * num_cus;
+  const int64_t per_split = (g_eff > 0 ? g_eff : 1) * p.k_tiles * kWaves;
+  int64_t S = (target_waves + per_split - 1) / per_split;
+  const int64_t max_s = (N + kWaves * kNB - 1) / (kWaves * kNB);
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  p.rows_per_split = (int)((N + S - 1) / S);
+  p.S = (int)((N + p.rows_per_split - 1) / p.rows_per_split);
+  return p;
+}
+
+size_t dgrad_workspace_bytes(const DgradPlan& p, int64_t M, int64_t K) {
+  return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)K * sizeof(float) : 0;
+}
+
+hipError_t launch_dgrad(const DgradArgs& g, const DgradPlan& p, hipStream_t stream) {
+  DgradKArgs a;
+  a.dy = g.dy;
+  a.packed = g.packed;
+  a.absmax = g.absmax;
+  a.sizes = g.sizes;
+  a.ids = g.ids;
+  a.dx = g.dx;
+  a.partial = g.partial;
+  a.E = g.E;
+  a.N = g.N;
+  a.K = g.K;
+  a.G = g.G;
+  a.M = g.M;
+  a.S = p.S;
+  a.rows_per_split = p.rows_per_split;
+  const unsigned slots = (unsigned)group_slots(g.G, g.M, 1);
+  if (slots == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.k_tiles, slots, (unsigned)p.S);
+  switch (p.R) {
+    case 1: hipLaunchKernelGGL(dgrad_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(dgrad_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(dgrad_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S == 1) return e;
+  const dim3 rgrid((unsigned)((g.K + 255) / 256), slots);
+  hipLaunchKernelGGL(dgrad_reduce_kernel, rgrid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace gnf4

@@ -211,6 +211,27 @@ hipError_t launch_row_exp(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int T, int M, int K,
                          uint16_t* out, hipStream_t stream);
 
+struct DgradArgs {
+  const uint16_t* dy;
+  const uint8_t* packed;
+  const float* absmax;
+  const int32_t* sizes;
+  const int32_t* ids;
+  uint16_t* dx;
+  float* partial;     // split-N partials [S, M, K]
+  int E, N, K, G, M;
+};
+
+struct DgradPlan {
+  int R;               // rows of dy per pass over the weights
+  int k_tiles;         // 2048-wide slices of K (one chunk per lane)
+  int S;               // N splits
+  int rows_per_split;  // weight rows per split
+};
+DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus);
+size_t dgrad_workspace_bytes(const DgradPlan& p, int64_t M, int64_t K);
+hipError_t launch_dgrad(const DgradArgs& a, const DgradPlan& p, hipStream_t stream);
+
 hipError_t launch_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
                          hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_rows, const float* topk_w,

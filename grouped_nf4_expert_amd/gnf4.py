@@ -60,6 +60,11 @@ def library():
     lib.gnf4_route_sort.restype = ctypes.c_int
     lib.gnf4_route_sort.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                     vp]
+    lib.gnf4_grouped_dgrad_workspace_size.restype = sz
+    lib.gnf4_grouped_dgrad_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.gnf4_grouped_dgrad.restype = ctypes.c_int
+    lib.gnf4_grouped_dgrad.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
+                                       vp]
     lib.gnf4_swiglu.restype = ctypes.c_int
     lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
     lib.gnf4_combine.restype = ctypes.c_int
@@ -180,6 +185,39 @@ def route_sort(logits, top_k, buffers=None):
         _ptr(r.num_groups), _ptr(buffers.workspace), buffers.ws_bytes, _stream()),
         "gnf4_route_sort")
     return r
+
+
+# ------------------------------------------------------------------ dgrad
+
+def grouped_dgrad(dy, packed, absmax, group_sizes, group_expert_ids, G=None, dx=None,
+                  workspace=None):
+    """dx[M, K] (bf16) = per-group dy[rows] @ dequant(W[expert]) -- the
+    activation gradient of grouped_gemm over the same packed stack."""
+    _need(dy, "dy", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(absmax, "absmax", torch.float32, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
+    M, N = dy.shape
+    E, N_w, half_k = packed.shape
+    K = 2 * half_k
+    if N_w != N or absmax.shape != (E, N, K // 64):
+        raise ValueError("packed/absmax shapes do not match dy's N")
+    if G is None:
+        G = min(group_sizes.numel(), M)
+    if G > group_sizes.numel() or G > group_expert_ids.numel():
+        raise ValueError("G exceeds the group arrays")
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    _need(dx, "dx", torch.bfloat16, 2)
+    need = library().gnf4_grouped_dgrad_workspace_size(M, N, K, G, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gnf4_grouped_dgrad(
+        _ptr(dy), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes), _ptr(group_expert_ids),
+        G, M, _ptr(dx), _ptr(workspace), ws_bytes, _stream()), "gnf4_grouped_dgrad")
+    return dx
 
 
 # ------------------------------------------------------------ swiglu / combine

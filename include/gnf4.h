@@ -153,6 +153,42 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
                              int32_t top_k, int64_t M, uint16_t* x_sorted, void* stream);
 
 /*
+ * gnf4_grouped_dgrad -- the activation gradient of the grouped GEMM over the
+ * same packed stack: dx[r, :] = dy[r, :] . dequant(W[expert_ids[g]]) for the
+ * rows r of each group g.
+ *
+ * Landing page "grouped-nf4-gemm", "Owns" (the grouped packed GEMM and its
+ * dgrad).  The contraction runs over N, across the rows of each expert's
+ * K-contiguous [N, K/2] codes.
+ *
+ *   dy                [M, N] bf16 bits: output gradient, rows grouped as for
+ *                     gnf4_grouped_gemm (2-byte aligned)
+ *   packed, absmax    [E, N, K/2] uint8 and [E, N, K/64] fp32 (as gnf4_pack writes)
+ *   group_sizes, group_expert_ids, G, M: as gnf4_grouped_gemm
+ *   dx                [M, K] bf16 bits out; only rows covered by a valid
+ *                     group are written
+ *   workspace         device scratch of gnf4_grouped_dgrad_workspace_size()
+ *                     bytes for the split-N fp32 partials (16-byte aligned);
+ *                     with less, the call runs unsplit (correct, slower)
+ *
+ * fp32 decode and accumulation, one bf16 rounding; |dx - exact| <= 8e-3
+ * |exact| + 1e-3 rms(exact) per element.  Splits are summed in fixed order:
+ * deterministic run to run.  Every weight byte is read once per pass of up
+ * to 4 rows of dy, so the kernel suits groups of few rows (decode-sized
+ * batches); large groups re-read the weights once per 4 rows.
+ * Limits: as gnf4_grouped_gemm, plus M * N < 2^31.
+ * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_UNSUPPORTED,
+ * GNF4_ERR_HIP.
+ */
+size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);
+
+gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const float* absmax,
+                               int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                               const int32_t* group_expert_ids, int64_t G, int64_t M,
+                               uint16_t* dx, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * gnf4_swiglu -- the activation between the two expert projections:
  * h[r, i] = silu(gate_up[r, i]) * gate_up[r, I + i] for r < M, i < I, with
  * silu(g) = g / (1 + exp(-g)).
