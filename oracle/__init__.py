@@ -43,14 +43,14 @@ byte round trips, exact-rational brute force, closed forms, invariants).
 """
 
 from .nf4 import (NF4_TABLE, ref_pack, ref_unpack, ref_codes, ref_quantize_block,
-                  ref_byte_ratio_vs_bf16)
+                  ref_byte_ratio_vs_bf16, ref_round_bf16)
 from .route import ref_topk, ref_sort, ref_route_sort
 from .gemm import ref_group_rows, ref_grouped_gemm, ref_grouped_gemm_entries, ref_grouped_dgrad
 from .moe import ref_silu, ref_swiglu, ref_combine, ref_expert_projection, ref_moe_ffn
 
 __all__ = [
     "NF4_TABLE", "ref_pack", "ref_unpack", "ref_codes", "ref_quantize_block",
-    "ref_byte_ratio_vs_bf16",
+    "ref_byte_ratio_vs_bf16", "ref_round_bf16",
     "ref_topk", "ref_sort", "ref_route_sort",
     "ref_group_rows", "ref_grouped_gemm", "ref_grouped_gemm_entries", "ref_grouped_dgrad",
     "ref_silu", "ref_swiglu", "ref_combine", "ref_expert_projection", "ref_moe_ffn",

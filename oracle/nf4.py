@@ -84,18 +84,44 @@ def ref_quantize_block(block):
     return codes, a
 
 
-def ref_pack(w):
+def ref_round_bf16(a):
+    """fp32 -> the nearest bf16 value (ties to even), saturating at the
+    largest finite bf16 instead of overflowing; returned as fp32 values.
+
+    bf16 keeps the top 16 bits of an fp32: adding 0x7FFF plus the lowest kept
+    bit to the bit pattern and truncating rounds to nearest, ties to even.
+    """
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    r = np.where((r & 0x7FFF) == 0x7F80, (r & 0x8000) | 0x7F7F, r)  # saturate
+    return (r.astype(np.uint32) << 16).view(np.float32)
+
+
+def ref_pack(w, absmax_dtype="f32"):
     """Quantise and pack ``w[..., N, K]`` (fp32 values) blockwise along K.
 
     Returns ``(packed uint8[..., N, K//2], absmax float32[..., N, K//64])``.
     Vectorised form of :func:`ref_quantize_block` applied to every block.
+
+    ``absmax_dtype="bf16"``: the 4.25-bit form (page "How do I run a MoE
+    whose experts do not fit in VRAM ...", "Supported scope": the NF4 bake
+    takes ``--absmax-dtype f32|bf16|auto``).  Reading: each
+    block's absmax is stored rounded to bf16 (nearest, ties to even,
+    saturating) and the codes are chosen against the stored value -- the
+    nearest level to x / a_stored, ties to the lower code, so decoding with
+    the stored absmax is the same rule as the fp32 form.  The absmax comes
+    back as fp32 values that bf16 holds exactly.  m_i * a_stored is still
+    exact in fp64 (26 + 8 significant bits).
     """
+    assert absmax_dtype in ("f32", "bf16")
     w = np.asarray(w, dtype=np.float32)
     K = w.shape[-1]
     assert K % BLOCK == 0, "K must be a multiple of the 64-element block"
     assert np.all(np.isfinite(w)), "non-finite weights are outside the contract"
     blocks = w.reshape(w.shape[:-1] + (K // BLOCK, BLOCK))
     absmax = np.max(np.abs(blocks), axis=-1).astype(np.float32)
+    if absmax_dtype == "bf16":
+        absmax = ref_round_bf16(absmax)
     thr_a = absmax.astype(np.float64)[..., None]
     x = blocks.astype(np.float64)
     codes = np.zeros(blocks.shape, dtype=np.uint8)

@@ -228,3 +228,51 @@ def test_census_shape_is_whole_blocks():
 def test_rejects_ragged_k():
     with pytest.raises(AssertionError):
         oracle.ref_pack(np.ones((1, 96), dtype=np.float32))
+
+
+# ----------------------------------------------------------- bf16 absmax
+
+def test_round_bf16_matches_torch_and_saturates():
+    import torch
+    rng = np.random.default_rng(71)
+    a = np.concatenate([rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.005859375, 3e-39, 1e-45],
+                                 np.float32)]).astype(np.float32)
+    got = oracle.ref_round_bf16(a)
+    want = torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(got, want)
+    big = np.array([3.39e38, np.finfo(np.float32).max, -np.finfo(np.float32).max], np.float32)
+    sat = oracle.ref_round_bf16(big)
+    assert np.all(np.isfinite(sat))
+    assert sat[1] == np.float32(3.3895313892515355e38) and sat[2] == -sat[1]
+
+
+def test_bf16_absmax_codes_are_nearest_to_the_stored_scale():
+    """Brute force: with the bf16-rounded absmax a_s stored, every code is the
+    exact-rational nearest level to x / a_s, ties to the lower code."""
+    from fractions import Fraction
+    rng = np.random.default_rng(73)
+    w = (rng.standard_normal((3, 128)) * 0.3).astype(np.float32)
+    w[1, :64] = np.float32(1.0039) * np.sign(rng.standard_normal(64)).astype(np.float32)
+    packed, absmax = oracle.ref_pack(w, absmax_dtype="bf16")
+    codes = oracle.ref_codes(packed)
+    levels = [Fraction(float(v)) for v in oracle.NF4_TABLE]
+    for n in range(3):
+        for b in range(2):
+            a_s = absmax[n, b]
+            assert a_s == oracle.ref_round_bf16(np.abs(w[n, 64 * b:64 * b + 64]).max())
+            for j in range(64):
+                x = Fraction(float(w[n, 64 * b + j])) / Fraction(float(a_s))
+                d = [abs(x - lv) for lv in levels]
+                best = min(d)
+                assert codes[n, 64 * b + j] == d.index(best)
+
+
+def test_bf16_absmax_saves_a_sixteenth_of_a_byte_per_weight():
+    w = np.random.default_rng(74).standard_normal((4, 256)).astype(np.float32)
+    _, a32 = oracle.ref_pack(w)
+    p16, a16 = oracle.ref_pack(w, absmax_dtype="bf16")
+    assert a16.shape == a32.shape
+    assert np.all(oracle.ref_round_bf16(a32) == a16)
+    # bits per weight: 4 + 16/64 with bf16 absmax, 4 + 32/64 with fp32
+    assert (p16.nbytes * 8 + a16.size * 16) / w.size == 4.25
