@@ -81,17 +81,27 @@ int gnf4_last_hip_error(void) { return g_last_hip_error; }
 
 const char* gnf4_version(void) { return "0.1.0"; }
 
+static bool valid_dtype(int32_t d) { return d == GNF4_DTYPE_BF16 || d == GNF4_DTYPE_F32; }
+static size_t dtype_bytes(int32_t d) { return d == GNF4_DTYPE_BF16 ? 2 : 4; }
+
 gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
                       uint8_t* packed, float* absmax, void* stream) {
+  return gnf4_pack_ex(w, w_dtype, E, N, K, packed, absmax, GNF4_DTYPE_F32, stream);
+}
+
+gnf4_status gnf4_pack_ex(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
+                         uint8_t* packed, void* absmax, int32_t absmax_dtype, void* stream) {
   if (!w || !packed || !absmax) return GNF4_ERR_INVALID_ARG;
   if (E <= 0 || N <= 0 || K <= 0 || K % kBlock != 0) return GNF4_ERR_INVALID_ARG;
-  if (w_dtype != GNF4_DTYPE_BF16 && w_dtype != GNF4_DTYPE_F32) return GNF4_ERR_INVALID_ARG;
-  if (!aligned(w, 16) || !aligned(packed, 4) || !aligned(absmax, 4)) return GNF4_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(packed, 4) || !aligned(absmax, dtype_bytes(absmax_dtype)))
+    return GNF4_ERR_INVALID_ARG;
   if (E > INT64_MAX / N || E * N > INT64_MAX / K) return GNF4_ERR_INVALID_ARG;
   if (!is_device_ptr(w) || !is_device_ptr(packed) || !is_device_ptr(absmax))
     return GNF4_ERR_NOT_DEVICE_PTR;
   const int64_t n_blocks = E * N * (K / kBlock);
-  const hipError_t e = launch_pack(w, w_dtype, n_blocks, packed, absmax, (hipStream_t)stream);
+  const hipError_t e = launch_pack(w, w_dtype, n_blocks, packed, absmax, absmax_dtype,
+                                   (hipStream_t)stream);
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
@@ -141,8 +151,8 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
-static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const float* absmax,
-                               int64_t E, int64_t N, int64_t K, const int32_t* sizes,
+static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const void* absmax,
+                               int32_t absmax_dtype, int64_t E, int64_t N, int64_t K, const int32_t* sizes,
                                const int32_t* ids, int64_t G, int64_t M, uint16_t* y,
                                void* ws, size_t ws_bytes, int32_t path, int32_t split_k,
                                void* stream, const int32_t* slots = nullptr, int32_t slot_div = 1,
@@ -158,7 +168,9 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
   if (slots && (T * slot_div >= ((int64_t)1 << 31) || T * K >= ((int64_t)1 << 31)))
     return GNF4_ERR_UNSUPPORTED;
   if (!x || !packed || !absmax || !sizes || !ids || !y) return GNF4_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(sizes, 4) ||
+  if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, dtype_bytes(absmax_dtype)) ||
+      !aligned(sizes, 4) ||
       !aligned(ids, 4) || !aligned(y, 2) || (slots && !aligned(slots, 4)))
     return GNF4_ERR_INVALID_ARG;
   const void* ptrs[] = {x, packed, absmax, sizes, ids, y};
@@ -173,6 +185,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const f
   a.x = x;
   a.packed = packed;
   a.absmax = absmax;
+  a.abs_bf16 = absmax_dtype == GNF4_DTYPE_BF16;
   a.sizes = sizes;
   a.ids = ids;
   a.y = y;
@@ -256,11 +269,11 @@ size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_
   return dgrad_workspace_bytes(plan_dgrad(M, N, K, G, device_cu_count()), M, K);
 }
 
-gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const float* absmax,
+gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const void* absmax,
                                int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                const int32_t* group_expert_ids, int64_t G, int64_t M,
                                uint16_t* dx, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int32_t absmax_dtype, void* stream) {
   if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
     return GNF4_ERR_INVALID_ARG;
   if (M == 0 || G == 0) return GNF4_OK;
@@ -269,7 +282,9 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
     return GNF4_ERR_UNSUPPORTED;
   if (!dy || !packed || !absmax || !group_sizes || !group_expert_ids || !dx)
     return GNF4_ERR_INVALID_ARG;
-  if (!aligned(dy, 2) || !aligned(dx, 2) || !aligned(packed, 16) || !aligned(absmax, 4) ||
+  if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(dy, 2) || !aligned(dx, 2) || !aligned(packed, 16) ||
+      !aligned(absmax, dtype_bytes(absmax_dtype)) ||
       !aligned(group_sizes, 4) || !aligned(group_expert_ids, 4))
     return GNF4_ERR_INVALID_ARG;
   const void* ptrs[] = {dy, packed, absmax, group_sizes, group_expert_ids, dx};
@@ -279,6 +294,7 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
   a.dy = dy;
   a.packed = packed;
   a.absmax = absmax;
+  a.abs_bf16 = absmax_dtype == GNF4_DTYPE_BF16;
   a.sizes = group_sizes;
   a.ids = group_expert_ids;
   a.dx = dx;
@@ -334,14 +350,16 @@ gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const floa
 }
 
 gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
-                                     int32_t top_k, const uint8_t* packed, const float* absmax,
+                                     int32_t top_k, const uint8_t* packed, const void* absmax,
                                      int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                      const int32_t* group_expert_ids, int64_t G, int64_t M,
                                      uint16_t* y, void* workspace, size_t workspace_bytes,
-                                     int32_t path, int32_t split_k, void* stream) {
+                                     int32_t path, int32_t split_k, int32_t absmax_dtype,
+                                     void* stream) {
   if (!sorted_slots) return GNF4_ERR_INVALID_ARG;
-  return gemm_common(x, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
-                     workspace, workspace_bytes, path, split_k, stream, sorted_slots, top_k, T);
+  return gemm_common(x, packed, absmax, absmax_dtype, E, N, K, group_sizes, group_expert_ids, G,
+                     M, y, workspace, workspace_bytes, path, split_k, stream, sorted_slots, top_k,
+                     T);
 }
 
 size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
@@ -364,18 +382,19 @@ gnf4_status gnf4_grouped_gemm(const uint16_t* x_sorted, const uint8_t* packed,
                               const int32_t* group_sizes, const int32_t* group_expert_ids,
                               int64_t G, int64_t M, uint16_t* y, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  return gemm_common(x_sorted, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
-                     workspace, workspace_bytes, 0, 0, stream);
+  return gemm_common(x_sorted, packed, absmax, GNF4_DTYPE_F32, E, N, K, group_sizes,
+                     group_expert_ids, G, M, y, workspace, workspace_bytes, 0, 0, stream);
 }
 
 gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed,
-                                 const float* absmax, int64_t E, int64_t N, int64_t K,
+                                 const void* absmax, int64_t E, int64_t N, int64_t K,
                                  const int32_t* group_sizes, const int32_t* group_expert_ids,
                                  int64_t G, int64_t M, uint16_t* y, void* workspace,
                                  size_t workspace_bytes, int32_t path, int32_t split_k,
-                                 void* stream) {
-  return gemm_common(x_sorted, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M, y,
-                     workspace, workspace_bytes, path, split_k, stream);
+                                 int32_t absmax_dtype, void* stream) {
+  return gemm_common(x_sorted, packed, absmax, absmax_dtype, E, N, K, group_sizes,
+                     group_expert_ids, G, M, y, workspace, workspace_bytes, path, split_k,
+                     stream);
 }
 
 }  // extern "C"

@@ -2,7 +2,9 @@
 //
 // Page "grouped-nf4-gemm -- single-launch W4A16 GEMM over fused NF4 MoE
 // expert stacks": opening section (one launch for all active experts, LUT
-// decode to fp32 in registers, blockwise fp32 absmax, fp32 accumulation, bf16
+// decode to fp32 in registers, blockwise fp32 absmax (or bf16: page "How do
+// I run a MoE whose experts do not fit in VRAM ...", "Supported scope", the
+// bake's --absmax-dtype), fp32 accumulation, bf16
 // epilogue); "Layout" (a decode GEMV path beside the M-tile path); "Status /
 // roadmap" (split-K for starved grids with a per-split work floor; one
 // universal launch rule rather than a per-shape table).
@@ -97,8 +99,8 @@ __device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
 }
 
-template <int NU>
-__device__ __forceinline__ void load_weights(const uint8_t* wexp, const float* aexp,
+template <int NU, typename AbsT>
+__device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* aexp,
                                              size_t row_bytes, int bpr, int N, int n_base, int c,
                                              bool valid, uint4 (&wq)[NU], float (&av)[NU]) {
 #pragma unroll
@@ -106,7 +108,7 @@ __device__ __forceinline__ void load_weights(const uint8_t* wexp, const float* a
     const int n = n_base + j;
     if (valid && n < N) {
       wq[j] = *reinterpret_cast<const uint4*>(wexp + (size_t)n * row_bytes + 16 * (size_t)c);
-      av[j] = aexp[(size_t)n * bpr + (c >> 1)];
+      av[j] = absmax_at(aexp, (size_t)n * bpr + (c >> 1));
     } else {
       wq[j] = make_uint4(0, 0, 0, 0);
       av[j] = 0.0f;
@@ -202,7 +204,7 @@ __device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
 // table when the gather is fused), (2) the first row chunk's activations,
 // (3) every weight chunk of the lane, step by step; the decode then consumes
 // the weights in the same order.
-template <int L, int NU, int R, int STEPS>
+template <int L, int NU, int R, int STEPS, typename AbsT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)gr.expert * N * row_bytes;
-  const float* aexp = a.g.absmax + (size_t)gr.expert * N * bpr;
+  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)gr.expert * N * bpr;
   const int c_begin = s * a.cps;
   const int c_end = min(c_begin + a.cps, a.cpr);
   const int ncs = max(c_end - c_begin, 0);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int c = c_begin + tl + st * L;
-    load_weights<NU>(wexp, aexp, row_bytes, bpr, N, n_base, c, c < c_end, wq[st], av[st]);
+    load_weights<NU, AbsT>(wexp, aexp, row_bytes, bpr, N, n_base, c, c < c_end, wq[st], av[st]);
   }
   stage.store(s_x, 0);
   for (int base = kXBatch * kThreads; base < R * stage.per_row; base += kXBatch * kThreads) {
@@ -385,36 +387,36 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
   }
 }
 
-template <int L, int NU, int R, int STEPS>
+template <int L, int NU, int R, int STEPS, typename AbsT>
 hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.n_tiles, (unsigned)group_slots(a.g.G, a.g.M, 1), (unsigned)p.S);
   const size_t lds = (size_t)R * (size_t)(p.cps + 1) * 128;
-  hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS>), grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS, AbsT>), grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 // rows per lane times activation rows at most kMaxLoads (accumulators)
-template <int L, int NU, int STEPS>
+template <int L, int NU, int STEPS, typename AbsT>
 hipError_t launch_R(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   if constexpr (NU * 4 <= kMaxLoads)
-    if (p.R == 4) return launch_one<L, NU, 4, STEPS>(a, p, stream);
+    if (p.R == 4) return launch_one<L, NU, 4, STEPS, AbsT>(a, p, stream);
   if constexpr (NU * 2 <= kMaxLoads)
-    if (p.R == 2) return launch_one<L, NU, 2, STEPS>(a, p, stream);
-  if (p.R == 1) return launch_one<L, NU, 1, STEPS>(a, p, stream);
+    if (p.R == 2) return launch_one<L, NU, 2, STEPS, AbsT>(a, p, stream);
+  if (p.R == 1) return launch_one<L, NU, 1, STEPS, AbsT>(a, p, stream);
   return hipErrorInvalidValue;
 }
 
 // (NU, steps) pairs with NU * steps <= kMaxLoads
-template <int L>
+template <int L, typename AbsT>
 hipError_t launch_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   switch (p.steps * 16 + p.NU) {
-    case 16 + 4: return launch_R<L, 4, 1>(a, p, stream);
-    case 16 + 2: return launch_R<L, 2, 1>(a, p, stream);
-    case 16 + 1: return launch_R<L, 1, 1>(a, p, stream);
-    case 32 + 2: return launch_R<L, 2, 2>(a, p, stream);
-    case 32 + 1: return launch_R<L, 1, 2>(a, p, stream);
-    case 48 + 1: return launch_R<L, 1, 3>(a, p, stream);
-    case 64 + 1: return launch_R<L, 1, 4>(a, p, stream);
+    case 16 + 4: return launch_R<L, 4, 1, AbsT>(a, p, stream);
+    case 16 + 2: return launch_R<L, 2, 1, AbsT>(a, p, stream);
+    case 16 + 1: return launch_R<L, 1, 1, AbsT>(a, p, stream);
+    case 32 + 2: return launch_R<L, 2, 2, AbsT>(a, p, stream);
+    case 32 + 1: return launch_R<L, 1, 2, AbsT>(a, p, stream);
+    case 48 + 1: return launch_R<L, 1, 3, AbsT>(a, p, stream);
+    case 64 + 1: return launch_R<L, 1, 4, AbsT>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -520,12 +522,22 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
   a.rows_per_block = p.rows_per_block;
   a.inv_slot_div = 1.0 / (double)(g.slot_div > 0 ? g.slot_div : 1);
   hipError_t err;
-  switch (p.L) {
-    case 64: err = launch_L<64>(a, p, stream); break;
-    case 32: err = launch_L<32>(a, p, stream); break;
-    case 16: err = launch_L<16>(a, p, stream); break;
-    case 8: err = launch_L<8>(a, p, stream); break;
-    default: return hipErrorInvalidValue;
+  if (g.abs_bf16) {
+    switch (p.L) {
+      case 64: err = launch_L<64, uint16_t>(a, p, stream); break;
+      case 32: err = launch_L<32, uint16_t>(a, p, stream); break;
+      case 16: err = launch_L<16, uint16_t>(a, p, stream); break;
+      case 8: err = launch_L<8, uint16_t>(a, p, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (p.L) {
+      case 64: err = launch_L<64, float>(a, p, stream); break;
+      case 32: err = launch_L<32, float>(a, p, stream); break;
+      case 16: err = launch_L<16, float>(a, p, stream); break;
+      case 8: err = launch_L<8, float>(a, p, stream); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   if (err != hipSuccess || p.S == 1) return err;
   const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)group_slots(g.G, g.M, 1));

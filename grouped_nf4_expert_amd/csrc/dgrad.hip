@@ -35,7 +35,7 @@ constexpr int kChunkPitch = 33;  // floats per lane in the reduction buffer (con
 struct DgradKArgs {
   const uint16_t* dy;   // [M, N] bf16
   const uint8_t* packed;
-  const float* absmax;
+  const void* absmax;   // fp32, or bf16 bits
   const int32_t* sizes;
   const int32_t* ids;
   uint16_t* dx;         // [M, K] bf16
@@ -57,7 +57,7 @@ __device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
 }
 
-template <int R>
+template <int R, typename AbsT>
 __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
   __shared__ float s_red[kWaves * kWave * kChunkPitch];
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   const int bpr = K / kBlock;
   const size_t row_bytes = (size_t)K / 2;
   const uint8_t* wexp = a.packed + (size_t)gr.expert * N * row_bytes;
-  const float* aexp = a.absmax + (size_t)gr.expert * N * bpr;
+  const AbsT* aexp = static_cast<const AbsT*>(a.absmax) + (size_t)gr.expert * N * bpr;
   const int s = blockIdx.z;
   const int n_begin = s * a.rows_per_split;
   const int n_end = min(n_begin + a.rows_per_split, N);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
         const bool ok = n < n_end;
         const int nn = ok ? n : n_begin;
         wq[b] = *reinterpret_cast<const uint4*>(wexp + (size_t)nn * row_bytes + 16 * (size_t)cc);
-        av[b] = (ok && c_ok) ? aexp[(size_t)nn * bpr + (cc >> 1)] : 0.0f;
+        av[b] = (ok && c_ok) ? absmax_at(aexp, (size_t)nn * bpr + (cc >> 1)) : 0.0f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int row = min(r0 + r, r_end - 1);
@@ -222,10 +222,18 @@ hipError_t launch_dgrad(const DgradArgs& g, const DgradPlan& p, hipStream_t stre
   const unsigned slots = (unsigned)group_slots(g.G, g.M, 1);
   if (slots == 0) return hipSuccess;
   const dim3 grid((unsigned)p.k_tiles, slots, (unsigned)p.S);
-  switch (p.R) {
-    case 1: hipLaunchKernelGGL(dgrad_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(dgrad_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL(dgrad_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+  if (g.abs_bf16) {
+    switch (p.R) {
+      case 1: hipLaunchKernelGGL((dgrad_kernel<1, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((dgrad_kernel<2, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((dgrad_kernel<4, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+  } else {
+    switch (p.R) {
+      case 1: hipLaunchKernelGGL((dgrad_kernel<1, float>), grid, dim3(kThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((dgrad_kernel<2, float>), grid, dim3(kThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((dgrad_kernel<4, float>), grid, dim3(kThreads), 0, stream, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;

@@ -46,6 +46,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// One block absmax as fp32, from either stored form (fp32, or bf16 bits).
+__device__ __forceinline__ float absmax_at(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float absmax_at(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -156,8 +162,9 @@ inline int64_t group_slots(int64_t G, int64_t M, int64_t lo) {
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the C-ABI layer before these are called.
 
+// absmax is fp32 (abs_dtype GNF4_DTYPE_F32) or bf16 bits (GNF4_DTYPE_BF16).
 hipError_t launch_pack(const void* w, int dtype, int64_t n_blocks, uint8_t* packed,
-                       float* absmax, hipStream_t stream);
+                       void* absmax, int abs_dtype, hipStream_t stream);
 
 struct RoutePlan {
   int chunk_tokens;   // tokens per chunk of the sort
@@ -175,7 +182,8 @@ hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32
 struct GemmArgs {
   const uint16_t* x;
   const uint8_t* packed;
-  const float* absmax;
+  const void* absmax;  // fp32, or bf16 bits when abs_bf16
+  bool abs_bf16;
   const int32_t* sizes;
   const int32_t* ids;
   uint16_t* y;
@@ -214,7 +222,8 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int
 struct DgradArgs {
   const uint16_t* dy;
   const uint8_t* packed;
-  const float* absmax;
+  const void* absmax;  // fp32, or bf16 bits when abs_bf16
+  bool abs_bf16;
   const int32_t* sizes;
   const int32_t* ids;
   uint16_t* dx;

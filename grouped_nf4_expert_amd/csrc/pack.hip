@@ -4,7 +4,11 @@
 // expert stacks", opening section: [E, N, K/2] uint8 codes (two per byte) and
 // one fp32 absmax per block, in the bitsandbytes gemm_4bit conventions;
 // "Cross-vendor projections": 3.56x smaller than bf16, i.e. 64-element blocks
-// with fp32 absmax.  Code values: QLoRA NormalFloat4.
+// with fp32 absmax.  Code values: QLoRA NormalFloat4.  Page "How do I run a
+// MoE whose experts do not fit in VRAM ...", "Supported scope": the bake
+// also stores the absmax as bf16 (4.25 bits per weight); then the block
+// maximum is rounded to bf16 (nearest, ties to even, saturating at the
+// largest finite bf16) and the codes are chosen against that stored value.
 //
 // A 64-element block never straddles a row (K % 64 == 0), so the stack is a
 // flat run of blocks: block b covers elements [64b, 64b + 64), bytes
@@ -35,11 +39,19 @@ __device__ __forceinline__ uint32_t code_of(float x, const double* thr, bool zer
   return c;
 }
 
-template <int DTYPE>
+// fp32 -> bf16 bits, nearest even, saturating at the largest finite bf16
+// (inputs are finite and non-negative here)
+__device__ __forceinline__ uint32_t bf16_rne_sat(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (r & 0x7fffu) == 0x7f80u ? (r & 0x8000u) | 0x7f7fu : r;
+}
+
+template <int DTYPE, bool ABS_BF16>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const void* __restrict__ w,
                                                             int64_t n_blocks,
                                                             uint8_t* __restrict__ packed,
-                                                            float* __restrict__ absmax) {
+                                                            void* __restrict__ absmax) {
   const int sub = threadIdx.x & 7;  // lane within the block's 8-lane group
   int64_t blk = ((int64_t)blockIdx.x * kPackThreads + threadIdx.x) >> 3;
   const int64_t stride = ((int64_t)gridDim.x * kPackThreads) >> 3;
@@ -67,6 +79,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const void* __restri
     m = fmaxf(m, __shfl_xor(m, 1, kWave));
     m = fmaxf(m, __shfl_xor(m, 2, kWave));
     m = fmaxf(m, __shfl_xor(m, 4, kWave));
+    uint32_t m_bits = 0;
+    if constexpr (ABS_BF16) {  // the stored (rounded) absmax sets the codes
+      m_bits = bf16_rne_sat(m);
+      m = __uint_as_float(m_bits << 16);
+    }
     double thr[15];
     const double md = (double)m;
 #pragma unroll
@@ -80,24 +97,39 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const void* __restri
       word |= ((hi << 4) | lo) << (8 * j);
     }
     *reinterpret_cast<uint32_t*>(packed + blk * 32 + sub * 4) = word;
-    if (sub == 0) absmax[blk] = m;
+    if (sub == 0) {
+      if constexpr (ABS_BF16)
+        static_cast<uint16_t*>(absmax)[blk] = (uint16_t)m_bits;
+      else
+        static_cast<float*>(absmax)[blk] = m;
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_pack(const void* w, int dtype, int64_t n_blocks, uint8_t* packed,
-                       float* absmax, hipStream_t stream) {
+                       void* absmax, int abs_dtype, hipStream_t stream) {
   const int64_t blocks_needed = (n_blocks * 8 + kPackThreads - 1) / kPackThreads;
   const int64_t cap = (int64_t)device_cu_count() * 64;
   const unsigned grid = (unsigned)(blocks_needed < cap ? blocks_needed : cap);
   if (grid == 0) return hipSuccess;
-  if (dtype == GNF4_DTYPE_BF16)
-    hipLaunchKernelGGL(pack_kernel<GNF4_DTYPE_BF16>, dim3(grid), dim3(kPackThreads), 0, stream,
-                       w, n_blocks, packed, absmax);
-  else
-    hipLaunchKernelGGL(pack_kernel<GNF4_DTYPE_F32>, dim3(grid), dim3(kPackThreads), 0, stream,
-                       w, n_blocks, packed, absmax);
+  const bool ab = abs_dtype == GNF4_DTYPE_BF16;
+  if (dtype == GNF4_DTYPE_BF16) {
+    if (ab)
+      hipLaunchKernelGGL((pack_kernel<GNF4_DTYPE_BF16, true>), dim3(grid), dim3(kPackThreads), 0,
+                         stream, w, n_blocks, packed, absmax);
+    else
+      hipLaunchKernelGGL((pack_kernel<GNF4_DTYPE_BF16, false>), dim3(grid), dim3(kPackThreads), 0,
+                         stream, w, n_blocks, packed, absmax);
+  } else {
+    if (ab)
+      hipLaunchKernelGGL((pack_kernel<GNF4_DTYPE_F32, true>), dim3(grid), dim3(kPackThreads), 0,
+                         stream, w, n_blocks, packed, absmax);
+    else
+      hipLaunchKernelGGL((pack_kernel<GNF4_DTYPE_F32, false>), dim3(grid), dim3(kPackThreads), 0,
+                         stream, w, n_blocks, packed, absmax);
+  }
   return hipGetLastError();
 }
 

@@ -151,7 +151,7 @@ struct PassCtx {
   _Float16* s_x;           // [2][kPassRows * kLdsRow]
   int* s_exp;              // [kPassRows] activation exponents of the pass's rows
   const uint8_t* wrow;     // this lane's weight row (or row 0 when out of range)
-  const float* arow;       // its absmax row
+  const void* arow;        // its absmax row (fp32, or bf16 bits)
   bool n_ok;               // the lane's column exists
   int sexp;                // its power-of-two scale exponent
   int tid, i, h, N, K, bpr, n, p0, rows, r_end, n_steps, rem_k;
@@ -172,7 +172,7 @@ __device__ __forceinline__ int div_slot(int n, int d) {
 // absent row or column reads an always-valid address) and what is absent is
 // dropped where the values are used: zero activations at staging, a zero
 // decode table for an absent weight block.
-template <int RT>
+template <int RT, typename AbsT>
 __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
   const GemmArgs& g = c.a->g;
   constexpr int kChunks = RT;  // 16-byte x chunks per thread: RT*32 rows x 16 chunks / 512 threads
@@ -240,7 +240,7 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
     const uint4* p = reinterpret_cast<const uint4*>(c.wrow + (ok ? 32 * (size_t)blk : 0));
     wc[sl][0] = p[0];
     wc[sl][1] = p[1];
-    wa[sl] = c.arow[ok ? blk : 0];
+    wa[sl] = absmax_at(static_cast<const AbsT*>(c.arow), ok ? blk : 0);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -311,6 +311,7 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
   }
 }
 
+template <typename AbsT>
 __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
   __shared__ int s_exp[kPassRows];
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
-  const float* aexp = a.g.absmax + (size_t)e * N * bpr;
+  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)e * N * bpr;
 
   // activation exponent of output row `row` (by token when the gather is
   // fused and the exponents were taken per token); the first pass's are
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   // of the same row, which leaves the maximum unchanged)
   float m = 0.0f;
   {
-    const float* ar = aexp + (n_ok ? (size_t)n * bpr : 0);
+    const AbsT* ar = aexp + (n_ok ? (size_t)n * bpr : 0);
     float mu[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) mu[u] = 0.0f;
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int bk = bk0 + 2 * u;
-        mu[u] = fmaxf(mu[u], ar[bk < bpr ? bk : h]);
+        mu[u] = fmaxf(mu[u], absmax_at(ar, bk < bpr ? bk : h));
       }
     }
 #pragma unroll
@@ -408,11 +409,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
     }
     const bool scaled = __syncthreads_or(t) != 0;
     switch ((c.rows + 31) / 32) {
-      case 1: tile_pass<1>(c, scaled); break;
-      case 2: tile_pass<2>(c, scaled); break;
-      case 3: tile_pass<3>(c, scaled); break;
-      case 4: tile_pass<4>(c, scaled); break;
-      default: tile_pass<5>(c, scaled); break;
+      case 1: tile_pass<1, AbsT>(c, scaled); break;
+      case 2: tile_pass<2, AbsT>(c, scaled); break;
+      case 3: tile_pass<3, AbsT>(c, scaled); break;
+      case 4: tile_pass<4, AbsT>(c, scaled); break;
+      default: tile_pass<5, AbsT>(c, scaled); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
@@ -492,7 +493,10 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   a.n_work = (int)group_slots(g.G, g.M, g.rows_min_tile) * a.n_tiles;
   const int grid = ((a.n_work + 7) / 8) * 8;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(tile_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (g.abs_bf16)
+    hipLaunchKernelGGL(tile_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(tile_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,8 @@ def library():
     lib.gnf4_version.argtypes = []
     lib.gnf4_pack.restype = ctypes.c_int
     lib.gnf4_pack.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.gnf4_pack_ex.restype = ctypes.c_int
+    lib.gnf4_pack_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp]
     lib.gnf4_route_sort_workspace_size.restype = sz
     lib.gnf4_route_sort_workspace_size.argtypes = [i64, i64, i32]
     lib.gnf4_route_sort.restype = ctypes.c_int
@@ -64,7 +66,7 @@ def library():
     lib.gnf4_grouped_dgrad_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.gnf4_grouped_dgrad.restype = ctypes.c_int
     lib.gnf4_grouped_dgrad.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
-                                       vp]
+                                       i32, vp]
     lib.gnf4_swiglu.restype = ctypes.c_int
     lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
     lib.gnf4_combine.restype = ctypes.c_int
@@ -79,10 +81,10 @@ def library():
     lib.gnf4_grouped_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz, vp]
     lib.gnf4_grouped_gemm_gather.restype = ctypes.c_int
     lib.gnf4_grouped_gemm_gather.argtypes = [vp, i64, vp, i32, vp, vp, i64, i64, i64, vp, vp, i64,
-                                             i64, vp, vp, sz, i32, i32, vp]
+                                             i64, vp, vp, sz, i32, i32, i32, vp]
     lib.gnf4_grouped_gemm_ex.restype = ctypes.c_int
     lib.gnf4_grouped_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp,
-                                         sz, i32, i32, vp]
+                                         sz, i32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -113,10 +115,20 @@ def _need(t, name, dtype, ndim=None):
 
 # ------------------------------------------------------------------- pack
 
-def pack(w, out=None):
+def _absmax_dtype(absmax):
+    if absmax.dtype == torch.float32:
+        return GNF4_DTYPE_F32
+    if absmax.dtype == torch.bfloat16:
+        return GNF4_DTYPE_BF16
+    raise TypeError("absmax must be float32 or bfloat16")
+
+
+def pack(w, out=None, absmax_dtype=torch.float32):
     """NF4-pack ``w`` [..., N, K] (bf16 or fp32 on the GPU).
 
-    Returns ``(packed uint8 [..., N, K/2], absmax fp32 [..., N, K/64])``.
+    Returns ``(packed uint8 [..., N, K/2], absmax [..., N, K/64])`` with the
+    absmax in ``absmax_dtype`` (float32, or bfloat16 for 4.25 bits/weight);
+    with ``out`` given, its absmax tensor's dtype decides.
     """
     if w.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("w must be bfloat16 or float32")
@@ -128,12 +140,12 @@ def pack(w, out=None):
     E = w.numel() // max(N * K, 1)
     if out is None:
         packed = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
-        absmax = torch.empty(w.shape[:-1] + (K // 64,), dtype=torch.float32, device=w.device)
+        absmax = torch.empty(w.shape[:-1] + (K // 64,), dtype=absmax_dtype, device=w.device)
     else:
         packed, absmax = out
     dt = GNF4_DTYPE_BF16 if w.dtype == torch.bfloat16 else GNF4_DTYPE_F32
-    _check(library().gnf4_pack(_ptr(w), dt, E, N, K, _ptr(packed), _ptr(absmax), _stream()),
-           "gnf4_pack")
+    _check(library().gnf4_pack_ex(_ptr(w), dt, E, N, K, _ptr(packed), _ptr(absmax),
+                                  _absmax_dtype(absmax), _stream()), "gnf4_pack_ex")
     return packed, absmax
 
 
@@ -195,7 +207,8 @@ def grouped_dgrad(dy, packed, absmax, group_sizes, group_expert_ids, G=None, dx=
     activation gradient of grouped_gemm over the same packed stack."""
     _need(dy, "dy", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 3)
-    _need(absmax, "absmax", torch.float32, 3)
+    _need(absmax, "absmax", absmax.dtype, 3)
+    adt = _absmax_dtype(absmax)
     _need(group_sizes, "group_sizes", torch.int32, 1)
     _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
     M, N = dy.shape
@@ -216,7 +229,7 @@ def grouped_dgrad(dy, packed, absmax, group_sizes, group_expert_ids, G=None, dx=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().gnf4_grouped_dgrad(
         _ptr(dy), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes), _ptr(group_expert_ids),
-        G, M, _ptr(dx), _ptr(workspace), ws_bytes, _stream()), "gnf4_grouped_dgrad")
+        G, M, _ptr(dx), _ptr(workspace), ws_bytes, adt, _stream()), "gnf4_grouped_dgrad")
     return dx
 
 
@@ -286,7 +299,8 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
     """
     _need(x_sorted, "x_sorted", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 3)
-    _need(absmax, "absmax", torch.float32, 3)
+    _need(absmax, "absmax", absmax.dtype, 3)
+    adt = _absmax_dtype(absmax)
     _need(group_sizes, "group_sizes", torch.int32, 1)
     _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
     rows, K = x_sorted.shape
@@ -311,11 +325,11 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
     if sorted_slots is None:
         _check(library().gnf4_grouped_gemm_ex(
             _ptr(x_sorted), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes),
-            _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes, path, split_k,
+            _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes, path, split_k, adt,
             _stream()), "gnf4_grouped_gemm")
     else:
         _check(library().gnf4_grouped_gemm_gather(
             _ptr(x_sorted), rows, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(absmax), E, N, K,
             _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
-            path, split_k, _stream()), "gnf4_grouped_gemm_gather")
+            path, split_k, adt, _stream()), "gnf4_grouped_gemm_gather")
     return y

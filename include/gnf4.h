@@ -94,6 +94,23 @@ gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int6
                       uint8_t* packed, float* absmax, void* stream);
 
 /*
+ * gnf4_pack_ex -- gnf4_pack with the absmax stored as fp32 (absmax_dtype =
+ * GNF4_DTYPE_F32, the same as gnf4_pack) or as bf16 (GNF4_DTYPE_BF16: 4.25
+ * bits per weight; page "How do I run a MoE whose experts do not fit in VRAM
+ * ...", "Supported scope": the NF4 bake's --absmax-dtype f32|bf16).
+ *
+ *   absmax  [E, N, K/64] out: fp32, or bf16 bits (2-byte aligned)
+ *
+ * With bf16, each block's maximum |w| is rounded to bf16 (nearest, ties to
+ * even, saturating at the largest finite bf16) and the codes are chosen
+ * against that stored value: the nearest level to x / a_stored, ties to the
+ * lower index, so decoding with the stored absmax follows the same rule.
+ * The GEMM entry points below take the absmax dtype with the stack.
+ */
+gnf4_status gnf4_pack_ex(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
+                         uint8_t* packed, void* absmax, int32_t absmax_dtype, void* stream);
+
+/*
  * gnf4_route_sort -- router top-k with softmax weights, then the
  * token->expert sort that yields (sizes, expert_ids).
  *
@@ -163,7 +180,8 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
  *
  *   dy                [M, N] bf16 bits: output gradient, rows grouped as for
  *                     gnf4_grouped_gemm (2-byte aligned)
- *   packed, absmax    [E, N, K/2] uint8 and [E, N, K/64] fp32 (as gnf4_pack writes)
+ *   packed, absmax    [E, N, K/2] uint8 and [E, N, K/64] fp32 or bf16 bits
+ *                     (`absmax_dtype`, as gnf4_pack_ex writes them)
  *   group_sizes, group_expert_ids, G, M: as gnf4_grouped_gemm
  *   dx                [M, K] bf16 bits out; only rows covered by a valid
  *                     group are written
@@ -182,11 +200,11 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
  */
 size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);
 
-gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const float* absmax,
+gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const void* absmax,
                                int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                const int32_t* group_expert_ids, int64_t G, int64_t M,
                                uint16_t* dx, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int32_t absmax_dtype, void* stream);
 
 /*
  * gnf4_swiglu -- the activation between the two expert projections:
@@ -291,7 +309,9 @@ gnf4_status gnf4_grouped_gemm(const uint16_t* x_sorted, const uint8_t* packed,
 
 /*
  * gnf4_grouped_gemm_ex -- gnf4_grouped_gemm with the path choice exposed, for
- * tests and tuning.  `path`: 0 = automatic (same as gnf4_grouped_gemm),
+ * tests and tuning, and the absmax stored as fp32 or bf16 (`absmax_dtype`,
+ * as gnf4_pack_ex writes it; `absmax` then points to fp32 or bf16 bits).
+ * `path`: 0 = automatic (same as gnf4_grouped_gemm),
  * 1 = every group on the decode path, 2 = every group on the tile path.
  * `split_k`: 0 = automatic, else the number of K splits of the decode path
  * (1..16; needs workspace of gnf4_grouped_gemm_workspace_size_ex();
@@ -302,11 +322,12 @@ size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int6
                                            int64_t E, int32_t path, int32_t split_k);
 
 gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed,
-                                 const float* absmax, int64_t E, int64_t N, int64_t K,
+                                 const void* absmax, int64_t E, int64_t N, int64_t K,
                                  const int32_t* group_sizes, const int32_t* group_expert_ids,
                                  int64_t G, int64_t M, uint16_t* y,
                                  void* workspace, size_t workspace_bytes,
-                                 int32_t path, int32_t split_k, void* stream);
+                                 int32_t path, int32_t split_k, int32_t absmax_dtype,
+                                 void* stream);
 
 /*
  * gnf4_grouped_gemm_gather -- gnf4_gather_rows fused into the grouped GEMM:
@@ -319,7 +340,7 @@ gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed
  *
  *   x             [T, K] bf16 bits: token activations (not grouped), 16-byte aligned
  *   sorted_slots  [M] int32 as gnf4_route_sort writes them; top_k >= 1
- *   other arguments as in gnf4_grouped_gemm_ex.
+ *   other arguments (absmax_dtype included) as in gnf4_grouped_gemm_ex.
  *
  * Same arithmetic and tolerance as gnf4_grouped_gemm applied to the gathered
  * rows; a row whose slot lies outside [0, T * top_k) is not written.
@@ -327,11 +348,12 @@ gnf4_status gnf4_grouped_gemm_ex(const uint16_t* x_sorted, const uint8_t* packed
  * sorted_slots or top_k < 1.
  */
 gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
-                                     int32_t top_k, const uint8_t* packed, const float* absmax,
+                                     int32_t top_k, const uint8_t* packed, const void* absmax,
                                      int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                      const int32_t* group_expert_ids, int64_t G, int64_t M,
                                      uint16_t* y, void* workspace, size_t workspace_bytes,
-                                     int32_t path, int32_t split_k, void* stream);
+                                     int32_t path, int32_t split_k, int32_t absmax_dtype,
+                                     void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

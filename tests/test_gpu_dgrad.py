@@ -124,3 +124,28 @@ def test_dgrad_dsv3_down_full_size_sampled_rows():
         o = host_f64(dy[idx]) @ w
         got = dx[idx]
         check_gemm(got, o, np.ones(rows.size, bool), f"dsv3 dgrad expert {e}")
+
+
+@pytest.mark.parametrize("name,gemm", [("olmoe", "down"), ("gptoss_t256", "down")])
+def test_dgrad_bf16_absmax(name, gemm):
+    wl = wls.WORKLOADS[name]
+    K, N = wl.gemm(gemm)
+    logits = wls.router_logits(wl)
+    ref = oracle.ref_route_sort(logits, wl.top_k)
+    r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
+    used = sorted(set(int(e) for e in ref["group_expert_ids"][: ref["num_groups"]]))
+    packed = torch.full((wl.E, N, K // 2), 0xFF, dtype=torch.uint8, device=DEV)
+    absmax = torch.full((wl.E, N, K // 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    p_ref = np.zeros((wl.E, N, K // 2), np.uint8)
+    a_ref = np.zeros((wl.E, N, K // 64), np.float32)
+    for e in used:
+        w = wls.expert_weights(wl, gemm, e)
+        gnf4.pack(bf16_dev(w), out=(packed[e], absmax[e]))
+        p_ref[e], a_ref[e] = oracle.ref_pack(w, absmax_dtype="bf16")
+    dy = bf16_dev(np.random.default_rng(9).standard_normal((wl.M, N)))
+    note(f"dgrad bf16 absmax {name}/{gemm}")
+    dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids)
+    torch.cuda.synchronize()
+    o, written = oracle.ref_grouped_dgrad(host_f64(dy), p_ref, a_ref, ref["group_sizes"],
+                                          ref["group_expert_ids"])
+    check_gemm(dx, o, written, f"dgrad bf16 absmax {name}/{gemm}")

@@ -204,6 +204,37 @@ def test_adversarial_absmax(scenario, path):
     check_gemm(y, c["y_ref"], c["written"], f"{scenario} path {path}")
 
 
+@pytest.mark.parametrize("name,gemm", [("olmoe", "gate_up"), ("gptoss", "down"),
+                                       ("gptoss_t256", "down"), ("qwen3_t8", "gate_up")])
+@pytest.mark.parametrize("path", [AUTO, DEC, TILE])
+def test_bf16_absmax(name, gemm, path):
+    """The 4.25-bit stack (absmax stored as bf16), both paths and the fused
+    gather, against the oracle's own bf16-absmax packing."""
+    wl = wls.WORKLOADS[name]
+    K, N = wl.gemm(gemm)
+    logits = wls.router_logits(wl)
+    ref = oracle.ref_route_sort(logits, wl.top_k)
+    r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
+    used = sorted(set(int(e) for e in ref["group_expert_ids"][: ref["num_groups"]]))
+    packed = torch.full((wl.E, N, K // 2), 0xFF, dtype=torch.uint8, device=DEV)
+    absmax = torch.full((wl.E, N, K // 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    p_ref = np.zeros((wl.E, N, K // 2), np.uint8)
+    a_ref = np.zeros((wl.E, N, K // 64), np.float32)
+    for e in used:
+        w = wls.expert_weights(wl, gemm, e)
+        gnf4.pack(bf16_dev(w), out=(packed[e], absmax[e]))
+        p_ref[e], a_ref[e] = oracle.ref_pack(w, absmax_dtype="bf16")
+    x_tok = wls.token_activations(wl, K)
+    x_host = x_tok[ref["sorted_slots"] // wl.top_k]
+    note(f"gemm bf16 absmax {name}/{gemm} path={path}")
+    y = gnf4.grouped_gemm(bf16_dev(x_tok), packed, absmax, r.group_sizes, r.group_expert_ids,
+                          path=path, sorted_slots=r.sorted_slots, top_k=wl.top_k)
+    torch.cuda.synchronize()
+    y_ref, written = oracle.ref_grouped_gemm(x_host, p_ref, a_ref, ref["group_sizes"],
+                                             ref["group_expert_ids"])
+    check_gemm(y, y_ref, written, f"bf16 absmax {name}/{gemm}/path{path}")
+
+
 @pytest.mark.parametrize("scale", [1e-6, 1e-20, 5e4, 1e30])
 @pytest.mark.parametrize("path", [DEC, TILE])
 def test_activation_magnitudes(scale, path):

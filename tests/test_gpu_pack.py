@@ -13,13 +13,15 @@ from gpu_util import DEV, bf16_dev, note
 pytestmark = pytest.mark.gpu
 
 
-def _compare(w_host, w_dev, what):
-    note(f"pack {what} shape={tuple(w_dev.shape)} dtype={w_dev.dtype}")
-    packed, absmax = gnf4.pack(w_dev)
+def _compare(w_host, w_dev, what, absmax_dtype="f32"):
+    note(f"pack {what} shape={tuple(w_dev.shape)} dtype={w_dev.dtype} absmax={absmax_dtype}")
+    tdt = torch.bfloat16 if absmax_dtype == "bf16" else torch.float32
+    packed, absmax = gnf4.pack(w_dev, absmax_dtype=tdt)
     torch.cuda.synchronize()
-    p_ref, a_ref = oracle.ref_pack(w_host)
+    assert absmax.dtype == tdt
+    p_ref, a_ref = oracle.ref_pack(w_host, absmax_dtype=absmax_dtype)
     p = packed.cpu().numpy()
-    a = absmax.cpu().numpy()
+    a = absmax.float().cpu().numpy()
     assert p.shape == p_ref.shape and a.shape == a_ref.shape
     bad = np.nonzero(p != p_ref)
     assert bad[0].size == 0, f"{what}: {bad[0].size} bytes differ, first at {tuple(b[0] for b in bad)}"
@@ -77,15 +79,39 @@ def _adversarial_rows():
     return np.stack(rows)[None]
 
 
-def test_pack_adversarial_fp32():
+@pytest.mark.parametrize("absmax_dtype", ["f32", "bf16"])
+def test_pack_adversarial_fp32(absmax_dtype):
     w = _adversarial_rows()
-    _compare(w, torch.from_numpy(w).to(DEV), "adversarial fp32")
+    _compare(w, torch.from_numpy(w).to(DEV), "adversarial fp32", absmax_dtype)
 
 
-def test_pack_adversarial_bf16():
+@pytest.mark.parametrize("absmax_dtype", ["f32", "bf16"])
+def test_pack_adversarial_bf16(absmax_dtype):
     from grouped_nf4_expert_amd.workloads import bf16_round
     w = bf16_round(_adversarial_rows())
-    _compare(w, bf16_dev(w), "adversarial bf16")
+    _compare(w, bf16_dev(w), "adversarial bf16", absmax_dtype)
+
+
+@pytest.mark.parametrize("name,gemm", [("olmoe", "gate_up"), ("gptoss", "down")])
+def test_pack_bf16_absmax_workload_experts(name, gemm):
+    """The 4.25-bit form: absmax rounded to bf16, codes against the stored value."""
+    wl = wls.WORKLOADS[name]
+    w = np.stack([wls.expert_weights(wl, gemm, e) for e in range(2)])
+    _compare(w, bf16_dev(w), f"{name}/{gemm}", "bf16")
+
+
+def test_pack_bf16_absmax_rounding_edges():
+    """Block maxima just below / at / above bf16 rounding midpoints, and
+    the saturation at the largest finite bf16."""
+    rng = np.random.default_rng(77)
+    rows = []
+    for m in (1.00390625, 1.0039, 1.0040, 1.01171875, 3.3895e38, 3.4e38, 1e-39, 7.5e-41):
+        r = (rng.uniform(-1, 1, 128) * np.float32(m)).astype(np.float32)
+        r[3] = np.float32(m)
+        r[70] = -np.float32(m)
+        rows.append(r)
+    w = np.stack(rows)[None]
+    _compare(w, torch.from_numpy(w).to(DEV), "bf16 absmax rounding edges", "bf16")
 
 
 def test_pack_full_size_expert_device_generated():

@@ -88,11 +88,11 @@ def test_route_rejects_bad_arguments(lib):
 def test_gemm_rejects_bad_arguments(lib):
     def call(**kw):
         a = dict(x=FAKE, p=FAKE, a=FAKE, E=4, N=64, K=128, s=FAKE, i=FAKE, G=2, M=8, y=FAKE,
-                 path=0, split=0)
+                 path=0, split=0, adt=1)
         a.update(kw)
         return lib.gnf4_grouped_gemm_ex(a["x"], a["p"], a["a"], a["E"], a["N"], a["K"], a["s"],
                                         a["i"], a["G"], a["M"], a["y"], NULL, 0, a["path"],
-                                        a["split"], NULL)
+                                        a["split"], a["adt"], NULL)
     assert call(K=96) == 1
     assert call(K=32) == 1
     assert call(N=0) == 1
@@ -103,6 +103,18 @@ def test_gemm_rejects_bad_arguments(lib):
     assert call(M=0) == 0     # nothing to do
     assert call(G=0) == 0
     assert call(x=ctypes.c_void_p(0x1004)) == 1   # x must be 16-byte aligned
+    assert call(adt=7) == 1                       # absmax dtype
+    assert call(a=ctypes.c_void_p(0x1002)) == 1   # fp32 absmax must be 4-byte aligned
+    # pack_ex(w, w_dtype, E, N, K, packed, absmax, absmax_dtype, stream)
+    assert lib.gnf4_pack_ex(FAKE, 0, 1, 1, 64, FAKE, FAKE, 5, NULL) == 1
+    assert lib.gnf4_pack_ex(FAKE, 0, 1, 1, 64, FAKE, ctypes.c_void_p(0x1001), 0, NULL) == 1
+    # dgrad(dy, packed, absmax, E, N, K, sizes, ids, G, M, dx, ws, ws_bytes, absmax_dtype, stream)
+    assert lib.gnf4_grouped_dgrad(FAKE, FAKE, FAKE, 4, 64, 96, FAKE, FAKE, 2, 8, FAKE, NULL, 0,
+                                  1, NULL) == 1   # K % 64
+    assert lib.gnf4_grouped_dgrad(FAKE, FAKE, FAKE, 4, 64, 128, FAKE, FAKE, 2, 0, FAKE, NULL, 0,
+                                  1, NULL) == 0   # M == 0
+    assert lib.gnf4_grouped_dgrad(FAKE, FAKE, FAKE, 4, 64, 128, FAKE, FAKE, 2, 8, FAKE, NULL, 0,
+                                  9, NULL) == 1   # absmax dtype
     assert lib.gnf4_gather_rows(FAKE, 4, 96, FAKE, 2, 8, FAKE, NULL) == 1
 
 
