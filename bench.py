@@ -35,10 +35,13 @@ MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 METRIC = "grouped NF4 GEMM effective HBM GB/s (decode) & TFLOP/s (prefill), % roofline"
 
 
+ABS_BYTES = 4  # bytes per block absmax: 4 (fp32) or 2 (bf16, --absmax-dtype bf16)
+
+
 def gemm_bytes(n_touched, M, N, K):
     """Algorithmic bytes of one grouped GEMM: each touched expert's codes and
     absmax once, the activations read once, the output written once."""
-    return n_touched * (N * K // 2 + 4 * N * K // 64) + 2 * M * K + 2 * M * N
+    return n_touched * (N * K // 2 + ABS_BYTES * N * K // 64) + 2 * M * K + 2 * M * N
 
 
 def swiglu_bytes(M, I):
@@ -69,6 +72,8 @@ def parse():
                     help="time the grouped dgrad alone at each workload's shapes into this JSONL")
     ap.add_argument("--glue", default="",
                     help="time the SwiGLU and top-k combine kernels alone into this JSONL")
+    ap.add_argument("--absmax-dtype", choices=("f32", "bf16"), default="f32",
+                    help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -116,9 +121,10 @@ def build_layers(wl, L, dev, first_layer=0):
     for li in range(first_layer, first_layer + L):
         ly = Layer()
         ly.pg = torch.empty((wl.E, Ng, Kg // 2), dtype=torch.uint8, device=dev)
-        ly.ag = torch.empty((wl.E, Ng, Kg // 64), dtype=torch.float32, device=dev)
+        adt = torch.bfloat16 if ABS_BYTES == 2 else torch.float32
+        ly.ag = torch.empty((wl.E, Ng, Kg // 64), dtype=adt, device=dev)
         ly.pd = torch.empty((wl.E, Nd, Kd // 2), dtype=torch.uint8, device=dev)
-        ly.ad = torch.empty((wl.E, Nd, Kd // 64), dtype=torch.float32, device=dev)
+        ly.ad = torch.empty((wl.E, Nd, Kd // 64), dtype=adt, device=dev)
         for e in range(wl.E):
             gnf4.pack(wls.expert_weights_device(wl, "gate_up", e, dev, li), out=(ly.pg[e], ly.ag[e]))
             gnf4.pack(wls.expert_weights_device(wl, "down", e, dev, li), out=(ly.pd[e], ly.ad[e]))
@@ -455,7 +461,9 @@ def summarize(d):
 
 
 def main():
+    global ABS_BYTES
     args = parse()
+    ABS_BYTES = 2 if args.absmax_dtype == "bf16" else 4
     if args.summarize:
         summarize(args.summarize)
         return
@@ -573,7 +581,7 @@ def main():
     dur_us = dominant_timed(10)
     avg_us = float(np.mean(dur_us))
     achieved = float(np.mean(dom_bytes)) / (avg_us * 1e-6) / 1e9
-    traffic = read_traffic(wl.name)
+    traffic = read_traffic(wl.name) if ABS_BYTES == 4 else None  # counters: fp32 stacks
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -597,7 +605,8 @@ def main():
             "workload": f"{wl.name}: E={wl.E} top_k={wl.top_k} T={wl.T} M={wl.M}, gate_up "
                         f"K={Kg} N={Ng} + down K={Kd} N={Nd}, {L} layers of distinct weights "
                         f"per step (route/sort + gate_up with fused gather + down)",
-            "weights": "NF4 (block 64, fp32 absmax)", "activations": "bf16",
+            "weights": f"NF4 (block 64, {'bf16' if ABS_BYTES == 2 else 'fp32'} absmax)",
+            "activations": "bf16",
             "global_batch": wl.T, "layers": L, "parallelism": "none (1 GPU)",
             "launch": "HIP graph per step" if args.graph else "host launches",
             "weight_sets": n_sets, "bytes_per_step": [int(b) for b in set_bytes],
