@@ -27,6 +27,10 @@ What the oracle computes, and the passage each step follows:
   Same README, opening section and "The claim" (fp32 accumulation, bf16
   epilogue, one launch for all active experts); and its dgrad (the
   activation gradient over the same packed stack, landing page "Owns").
+* ``mxfp4`` -- the grouped GEMM over MXFP4 stacks (E2M1 codes with E8M0
+  scales per 32 elements), the second packed format the landing page's
+  grouped GEMM serves ("Owns", "Use this when"); the formats' definitions
+  come from the OCP Microscaling specification.
 * ``moe``   -- the steps on either side of the GEMM: the SwiGLU activation
   between the two expert projections and the weighted top-k combine after
   the down projection (landing page "grouped-nf4-gemm", "Owns" and "Use this
@@ -47,6 +51,8 @@ from .nf4 import (NF4_TABLE, ref_pack, ref_unpack, ref_codes, ref_quantize_block
 from .route import ref_topk, ref_sort, ref_route_sort
 from .gemm import ref_group_rows, ref_grouped_gemm, ref_grouped_gemm_entries, ref_grouped_dgrad
 from .moe import ref_silu, ref_swiglu, ref_combine, ref_expert_projection, ref_moe_ffn
+from .mxfp4 import (E2M1_TABLE, ref_e2m1_value, ref_e8m0_value, ref_mx_codes, ref_mx_unpack,
+                    ref_grouped_gemm_mxfp4)
 
 __all__ = [
     "NF4_TABLE", "ref_pack", "ref_unpack", "ref_codes", "ref_quantize_block",
@@ -54,4 +60,6 @@ __all__ = [
     "ref_topk", "ref_sort", "ref_route_sort",
     "ref_group_rows", "ref_grouped_gemm", "ref_grouped_gemm_entries", "ref_grouped_dgrad",
     "ref_silu", "ref_swiglu", "ref_combine", "ref_expert_projection", "ref_moe_ffn",
+    "E2M1_TABLE", "ref_e2m1_value", "ref_e8m0_value", "ref_mx_codes", "ref_mx_unpack",
+    "ref_grouped_gemm_mxfp4",
 ]
