@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--workload", default="olmoe")
     ap.add_argument("--layers", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--cells", default="", help="also time every workload's GEMMs into this JSONL")
+    ap.add_argument("--mxfp4", default="",
+                    help="time the MXFP4 grouped GEMM alone at the decode shapes into this JSONL")
     ap.add_argument("--dgrad", default="",
                     help="time the grouped dgrad alone at each workload's shapes into this JSONL")
     ap.add_argument("--glue", default="",
@@ -336,6 +338,69 @@ def time_dgrad(path, dev):
     out.close()
 
 
+def time_mxfp4(path, dev):
+    """gnf4_grouped_gemm_mxfp4 alone at the decode shapes (GPT-OSS first: the
+    family released in MXFP4), cycling over enough random E2M1/E8M0 stack
+    copies to defeat the Infinity Cache; per-launch HIP events over a graph
+    of back-to-back launches with the fused gather.  Algorithmic bytes: each
+    touched expert's codes (N*K/2) and scales (N*K/32) once, the activation
+    rows read once, the output written once."""
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    out = open(path, "w")
+    cells = (("gptoss", "gate_up"), ("gptoss", "down"), ("olmoe", "gate_up"), ("olmoe", "down"),
+             ("qwen3_t8", "gate_up"))
+    for name, gemm in cells:
+        wl = wls.WORKLOADS[name]
+        r = gnf4.route_sort(torch.from_numpy(wls.router_logits(wl)).to(dev), wl.top_k)
+        G = min(wl.E, wl.M)
+        ng = int(r.num_groups.cpu()[0])
+        K, N = wl.gemm(gemm)
+        stack_bytes = wl.E * (N * K // 2 + N * K // 32)
+        copies = max(1, min(8, int(np.ceil(600e6 / stack_bytes))))
+        gen = torch.Generator(device=dev).manual_seed(17)
+        stacks = [(torch.randint(0, 256, (wl.E, N, K // 2), dtype=torch.uint8, device=dev,
+                                 generator=gen),
+                   torch.randint(118, 131, (wl.E, N, K // 32), dtype=torch.uint8, device=dev,
+                                 generator=gen)) for _ in range(copies)]
+        x = wls.activations_device(wl.T, K, dev, wl.seed, 70, K)
+        y = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(gnf4.gemm_workspace_size(wl.M, N, K, G, wl.E, gnf4.PATH_DECODE), 16),
+                         dtype=torch.uint8, device=dev)
+        per = 4 * copies
+
+        def launches():
+            for i in range(per):
+                p, sc = stacks[i % copies]
+                gnf4.grouped_gemm_mxfp4(x, p, sc, r.group_sizes, r.group_expert_ids, G=G, y=y,
+                                        workspace=ws, sorted_slots=r.sorted_slots, top_k=wl.top_k)
+        graph = capture(launches)
+        reps = 10
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            evs[i][0].record()
+            graph.replay()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        us = sorted(s_.elapsed_time(e_) * 1e3 / per for s_, e_ in evs)
+        med = us[len(us) // 2]
+        byt = ng * (N * K // 2 + N * K // 32) + 2 * wl.M * K + 2 * wl.M * N
+        rec = {"kernel": "mxfp4 grouped GEMM (decode path, fused gather)", "workload": name,
+               "gemm": gemm, "M": wl.M, "N": N, "K": K, "touched_experts": ng,
+               "median_us": round(med, 2), "GBps": round(byt / med / 1e3, 1),
+               "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": copies}
+        out.write(json.dumps(rec) + "\n")
+        out.flush()
+        print(f"[mxfp4] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del stacks
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def time_glue(path, dev, reps=10):
     """gnf4_swiglu and gnf4_combine alone at the decode (OLMoE, T=1) and
     prefill (DSV3, T=4096) shapes of the MoE layer: back-to-back launches
@@ -484,6 +549,9 @@ def main():
         return
     if args.dgrad:
         time_dgrad(args.dgrad, dev)
+        return
+    if args.mxfp4:
+        time_mxfp4(args.mxfp4, dev)
         return
 
     if args.copy_mb:

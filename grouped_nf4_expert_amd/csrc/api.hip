@@ -82,7 +82,11 @@ int gnf4_last_hip_error(void) { return g_last_hip_error; }
 const char* gnf4_version(void) { return "0.1.0"; }
 
 static bool valid_dtype(int32_t d) { return d == GNF4_DTYPE_BF16 || d == GNF4_DTYPE_F32; }
-static size_t dtype_bytes(int32_t d) { return d == GNF4_DTYPE_BF16 ? 2 : 4; }
+// scale kind of an MXFP4 stack inside gemm_common: E8M0 bytes, one per 32 codes
+constexpr int32_t kScaleE8M0 = 2;
+static size_t dtype_bytes(int32_t d) {
+  return d == GNF4_DTYPE_BF16 ? 2 : d == kScaleE8M0 ? 1 : 4;
+}
 
 gnf4_status gnf4_pack(const void* w, int32_t w_dtype, int64_t E, int64_t N, int64_t K,
                       uint8_t* packed, float* absmax, void* stream) {
@@ -168,7 +172,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
   if (slots && (T * slot_div >= ((int64_t)1 << 31) || T * K >= ((int64_t)1 << 31)))
     return GNF4_ERR_UNSUPPORTED;
   if (!x || !packed || !absmax || !sizes || !ids || !y) return GNF4_ERR_INVALID_ARG;
-  if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  if (!valid_dtype(absmax_dtype) && absmax_dtype != kScaleE8M0) return GNF4_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, dtype_bytes(absmax_dtype)) ||
       !aligned(sizes, 4) ||
       !aligned(ids, 4) || !aligned(y, 2) || (slots && !aligned(slots, 4)))
@@ -186,6 +190,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
   a.packed = packed;
   a.absmax = absmax;
   a.abs_bf16 = absmax_dtype == GNF4_DTYPE_BF16;
+  a.mxfp4 = absmax_dtype == kScaleE8M0;
   a.sizes = sizes;
   a.ids = ids;
   a.y = y;
@@ -318,6 +323,22 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
   }
   const hipError_t e = launch_dgrad(a, p, (hipStream_t)stream);
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
+                                    int32_t top_k, const uint8_t* packed, const uint8_t* scales,
+                                    int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                    const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                    uint16_t* y, void* workspace, size_t workspace_bytes,
+                                    int32_t split_k, void* stream) {
+  if (sorted_slots) {
+    if (top_k < 1 || T < 0) return GNF4_ERR_INVALID_ARG;
+    return gemm_common(x, packed, scales, kScaleE8M0, E, N, K, group_sizes, group_expert_ids, G,
+                       M, y, workspace, workspace_bytes, 1, split_k, stream, sorted_slots, top_k,
+                       T);
+  }
+  return gemm_common(x, packed, scales, kScaleE8M0, E, N, K, group_sizes, group_expert_ids, G, M,
+                     y, workspace, workspace_bytes, 1, split_k, stream);
 }
 
 gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,

@@ -38,6 +38,8 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "gnf4_internal.h"
 
 namespace gnf4 {
@@ -99,6 +101,27 @@ __device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
 }
 
+// The stack's scale type also names its format: fp32 or bf16 block absmax
+// (NF4 codes, 64 per block), or uint8 E8M0 scales (MXFP4: E2M1 codes, one
+// scale per 32 codes, i.e. per 16-byte chunk).
+template <typename AbsT>
+constexpr bool kMxfp4 = std::is_same_v<AbsT, uint8_t>;
+
+// E8M0 scale byte -> 2^(s - 127) in fp32 (2^-127 is a subnormal); 0xFF is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 255u ? 0x7fc00000u : s == 0u ? 0x00400000u : s << 23);
+}
+
+// Both E2M1 codes of byte B of d as fp32: .x from the low nibble (the first
+// element), .y from the high nibble.
+template <int B>
+__device__ __forceinline__ void e2m1_pair(uint32_t d, float& first, float& second) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, B);
+  first = v.x;
+  second = v.y;
+}
+
 template <int NU, typename AbsT>
 __device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* aexp,
                                              size_t row_bytes, int bpr, int N, int n_base, int c,
@@ -108,7 +131,10 @@ __device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* ae
     const int n = n_base + j;
     if (valid && n < N) {
       wq[j] = *reinterpret_cast<const uint4*>(wexp + (size_t)n * row_bytes + 16 * (size_t)c);
-      av[j] = absmax_at(aexp, (size_t)n * bpr + (c >> 1));
+      if constexpr (kMxfp4<AbsT>)
+        av[j] = e8m0_to_f32(aexp[(size_t)n * (2 * bpr) + c]);  // one scale per chunk
+      else
+        av[j] = absmax_at(aexp, (size_t)n * bpr + (c >> 1));
     } else {
       wq[j] = make_uint4(0, 0, 0, 0);
       av[j] = 0.0f;
@@ -228,7 +254,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)gr.expert * N * row_bytes;
-  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)gr.expert * N * bpr;
+  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) +
+                    (size_t)gr.expert * N * (kMxfp4<AbsT> ? 2 * bpr : bpr);
   const int c_begin = s * a.cps;
   const int c_end = min(c_begin + a.cps, a.cpr);
   const int ncs = max(c_end - c_begin, 0);
@@ -311,27 +338,41 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
         for (int j = 0; j < NU; ++j) {
           const uint32_t d = w == 0 ? wq[st][j].x : w == 1 ? wq[st][j].y
                            : w == 2 ? wq[st][j].z : wq[st][j].w;
-          // LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
-          // byte b hold its high code; after a left shift by 3, its low code.
-          const uint32_t dh = d >> 1;
-          const uint32_t dl = d << 3;
-          uint32_t oh[4], ol[4];
-          oh[0] = byte_and<0>(dh, 0x78u);
-          oh[1] = byte_and<1>(dh, 0x78u);
-          oh[2] = byte_and<2>(dh, 0x78u);
-          oh[3] = byte_and<3>(dh, 0x78u);
-          ol[0] = byte_and<0>(dl, 0x78u);
-          ol[1] = byte_and<1>(dl, 0x78u);
-          ol[2] = byte_and<2>(dl, 0x78u);
-          ol[3] = byte_and<3>(dl, 0x78u);
+          // the two elements of each byte: vh the first, vl the second
+          float vh[4], vl[4];
+          if constexpr (kMxfp4<AbsT>) {
+            // E2M1 through the hardware convert (first element = low nibble)
+            e2m1_pair<0>(d, vh[0], vl[0]);
+            e2m1_pair<1>(d, vh[1], vl[1]);
+            e2m1_pair<2>(d, vh[2], vl[2]);
+            e2m1_pair<3>(d, vh[3], vl[3]);
+          } else {
+            // NF4 LUT byte offsets 8 * code: after a right shift by 1, bits
+            // 3..6 of byte b hold its high code (the first element); after a
+            // left shift by 3, its low code.
+            const uint32_t dh = d >> 1;
+            const uint32_t dl = d << 3;
+            uint32_t oh[4], ol[4];
+            oh[0] = byte_and<0>(dh, 0x78u);
+            oh[1] = byte_and<1>(dh, 0x78u);
+            oh[2] = byte_and<2>(dh, 0x78u);
+            oh[3] = byte_and<3>(dh, 0x78u);
+            ol[0] = byte_and<0>(dl, 0x78u);
+            ol[1] = byte_and<1>(dl, 0x78u);
+            ol[2] = byte_and<2>(dl, 0x78u);
+            ol[3] = byte_and<3>(dl, 0x78u);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              vh[b] = lut_at(lut, oh[b]);
+              vl[b] = lut_at(lut, ol[b]);
+            }
+          }
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const float vh = lut_at(lut, oh[b]);
-            const float vl = lut_at(lut, ol[b]);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-              pr[j][r] = fmaf(xw[r][2 * b], vh, pr[j][r]);
-              pr[j][r] = fmaf(xw[r][2 * b + 1], vl, pr[j][r]);
+              pr[j][r] = fmaf(xw[r][2 * b], vh[b], pr[j][r]);
+              pr[j][r] = fmaf(xw[r][2 * b + 1], vl[b], pr[j][r]);
             }
           }
         }
@@ -522,7 +563,15 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
   a.rows_per_block = p.rows_per_block;
   a.inv_slot_div = 1.0 / (double)(g.slot_div > 0 ? g.slot_div : 1);
   hipError_t err;
-  if (g.abs_bf16) {
+  if (g.mxfp4) {
+    switch (p.L) {
+      case 64: err = launch_L<64, uint8_t>(a, p, stream); break;
+      case 32: err = launch_L<32, uint8_t>(a, p, stream); break;
+      case 16: err = launch_L<16, uint8_t>(a, p, stream); break;
+      case 8: err = launch_L<8, uint8_t>(a, p, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (g.abs_bf16) {
     switch (p.L) {
       case 64: err = launch_L<64, uint16_t>(a, p, stream); break;
       case 32: err = launch_L<32, uint16_t>(a, p, stream); break;

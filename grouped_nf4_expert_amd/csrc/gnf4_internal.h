@@ -182,8 +182,9 @@ hipError_t launch_route_sort(const float* logits, int T, int E, int top_k, int32
 struct GemmArgs {
   const uint16_t* x;
   const uint8_t* packed;
-  const void* absmax;  // fp32, or bf16 bits when abs_bf16
+  const void* absmax;  // fp32, or bf16 bits when abs_bf16; E8M0 bytes when mxfp4
   bool abs_bf16;
+  bool mxfp4;          // MXFP4 stack: E2M1 codes (first element low), E8M0 per 32
   const int32_t* sizes;
   const int32_t* ids;
   uint16_t* y;

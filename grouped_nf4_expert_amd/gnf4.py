@@ -67,6 +67,9 @@ def library():
     lib.gnf4_grouped_dgrad.restype = ctypes.c_int
     lib.gnf4_grouped_dgrad.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
                                        i32, vp]
+    lib.gnf4_grouped_gemm_mxfp4.restype = ctypes.c_int
+    lib.gnf4_grouped_gemm_mxfp4.argtypes = [vp, i64, vp, i32, vp, vp, i64, i64, i64, vp, vp, i64,
+                                            i64, vp, vp, sz, i32, vp]
     lib.gnf4_swiglu.restype = ctypes.c_int
     lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
     lib.gnf4_combine.restype = ctypes.c_int
@@ -197,6 +200,40 @@ def route_sort(logits, top_k, buffers=None):
         _ptr(r.num_groups), _ptr(buffers.workspace), buffers.ws_bytes, _stream()),
         "gnf4_route_sort")
     return r
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def grouped_gemm_mxfp4(x, packed, scales, group_sizes, group_expert_ids, G=None, y=None,
+                       workspace=None, split_k=0, sorted_slots=None, top_k=1):
+    """y[M, N] (bf16) over an MXFP4 stack: ``packed`` [E, N, K/2] uint8 E2M1
+    codes (element 2j in the low nibble), ``scales`` [E, N, K/32] uint8 E8M0.
+    With ``sorted_slots`` the gather is fused as in grouped_gemm."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(scales, "scales", torch.uint8, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
+    rows, K = x.shape
+    M = rows if sorted_slots is None else sorted_slots.numel()
+    if sorted_slots is not None:
+        _need(sorted_slots, "sorted_slots", torch.int32, 1)
+    E, N, half_k = packed.shape
+    if half_k * 2 != K or scales.shape != (E, N, K // 32):
+        raise ValueError("packed/scales shapes do not match x's K")
+    if G is None:
+        G = min(group_sizes.numel(), M)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = gemm_workspace_size(M, N, K, G, E, PATH_DECODE, split_k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gnf4_grouped_gemm_mxfp4(
+        _ptr(x), rows, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(scales), E, N, K,
+        _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
+        split_k, _stream()), "gnf4_grouped_gemm_mxfp4")
+    return y
 
 
 # ------------------------------------------------------------------ dgrad

@@ -170,6 +170,37 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
                              int32_t top_k, int64_t M, uint16_t* x_sorted, void* stream);
 
 /*
+ * gnf4_grouped_gemm_mxfp4 -- the grouped GEMM over an MXFP4 expert stack
+ * (E2M1 codes with one E8M0 scale per 32 elements along K), served from the
+ * checkpoint's own bytes: y = x . W[expert_ids[g]]^T per group.
+ *
+ * Landing page "grouped-nf4-gemm", "Owns" (the grouped packed GEMM over NF4
+ * and native MXFP4) and "Use this when" (MoEs released as MXFP4 -- e2m1 +
+ * e8m0 -- served without re-quantising).  Formats: OCP Microscaling.
+ *
+ *   x             [M, K] bf16 bits grouped by expert (sorted_slots NULL), or
+ *                 [T, K] token rows read through sorted_slots (fused gather)
+ *   packed        [E, N, K/2] uint8: E2M1 codes, element 2j in the LOW nibble
+ *                 of byte j (16-byte aligned)
+ *   scales        [E, N, K/32] uint8 E8M0: scale 2^(s - 127); 0xFF is NaN
+ *   other arguments as in gnf4_grouped_gemm_gather / gnf4_grouped_gemm_ex;
+ *   workspace     gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, 1, split_k)
+ *
+ * Codes are decoded by gfx950's E2M1 convert and each 32-code partial sum,
+ * accumulated in fp32, is multiplied by its block scale; bf16 output within
+ * the GEMM's tolerance.  All groups run on the decode path (there is no
+ * matrix-core MXFP4 path yet), so it suits decode-sized groups; large groups
+ * are correct but re-read each expert's codes once per 4 rows.
+ * Limits and errors: as gnf4_grouped_gemm_gather (K % 64 == 0).
+ */
+gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
+                                    int32_t top_k, const uint8_t* packed, const uint8_t* scales,
+                                    int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                    const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                    uint16_t* y, void* workspace, size_t workspace_bytes,
+                                    int32_t split_k, void* stream);
+
+/*
  * gnf4_grouped_dgrad -- the activation gradient of the grouped GEMM over the
  * same packed stack: dx[r, :] = dy[r, :] . dequant(W[expert_ids[g]]) for the
  * rows r of each group g.

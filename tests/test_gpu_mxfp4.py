@@ -1,0 +1,158 @@
+"""GPU parity for gnf4_grouped_gemm_mxfp4 against the fp64 MXFP4 oracle:
+random E2M1 code bytes and E8M0 scales (any byte is a valid code pair), the
+workloads' shapes with and without the fused gather, K splits, the grouping
+boundary cases, scale edge values (2^-127, 2^127, NaN) and GPT-OSS's whole
+stack (the model family released in MXFP4).
+
+Bar: |y - o| <= 8e-3 |o| + 1e-3 rms(o), as the NF4 GEMM.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_nf4_expert_amd import gnf4
+from grouped_nf4_expert_amd import workloads as wls
+
+from gpu_util import DEV, bf16_dev, check_gemm, host_f64, note
+from test_gpu_gemm import BOUNDARY_CASES
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(E, N, K, seed, lo=118, hi=131):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    packed = torch.randint(0, 256, (E, N, K // 2), dtype=torch.uint8, device=DEV, generator=g)
+    scales = torch.randint(lo, hi, (E, N, K // 32), dtype=torch.uint8, device=DEV, generator=g)
+    return packed, scales
+
+
+def _oracle(x_host, packed, scales, sizes, ids):
+    return oracle.ref_grouped_gemm_mxfp4(x_host, packed.cpu().numpy(), scales.cpu().numpy(),
+                                         sizes, ids)
+
+
+@pytest.mark.parametrize("name,gemm", [("tiny", "w"), ("olmoe", "gate_up"), ("olmoe", "down"),
+                                       ("qwen3_t8", "gate_up"), ("gptoss", "gate_up"),
+                                       ("gptoss", "down"), ("gptoss_t256", "down")])
+@pytest.mark.parametrize("gather", [False, True])
+def test_mxfp4_workload_shapes(name, gemm, gather):
+    wl = wls.WORKLOADS[name]
+    K, N = wl.gemm(gemm)
+    logits = wls.router_logits(wl)
+    ref = oracle.ref_route_sort(logits, wl.top_k)
+    r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
+    packed, scales = _stack(wl.E, N, K, seed=K + N)
+    x_tok = wls.token_activations(wl, K)
+    x_host = x_tok[ref["sorted_slots"] // wl.top_k]
+    note(f"mxfp4 {name}/{gemm} gather={gather}")
+    if gather:
+        y = gnf4.grouped_gemm_mxfp4(bf16_dev(x_tok), packed, scales, r.group_sizes,
+                                    r.group_expert_ids, sorted_slots=r.sorted_slots,
+                                    top_k=wl.top_k)
+    else:
+        xs = gnf4.gather_rows(bf16_dev(x_tok), r.sorted_slots, wl.top_k)
+        y = gnf4.grouped_gemm_mxfp4(xs, packed, scales, r.group_sizes, r.group_expert_ids)
+    torch.cuda.synchronize()
+    o, written = _oracle(x_host, packed, scales, ref["group_sizes"], ref["group_expert_ids"])
+    check_gemm(y, o, written, f"mxfp4 {name}/{gemm}")
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5])
+def test_mxfp4_split_k(split_k):
+    wl = wls.WORKLOADS["gptoss"]
+    K, N = wl.gemm("down")
+    logits = wls.router_logits(wl)
+    ref = oracle.ref_route_sort(logits, wl.top_k)
+    r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
+    packed, scales = _stack(wl.E, N, K, seed=7)
+    x = bf16_dev(np.random.default_rng(7).standard_normal((wl.M, K)))
+    note(f"mxfp4 split_k={split_k}")
+    y = gnf4.grouped_gemm_mxfp4(x, packed, scales, r.group_sizes, r.group_expert_ids,
+                                split_k=split_k)
+    torch.cuda.synchronize()
+    o, written = _oracle(host_f64(x), packed, scales, ref["group_sizes"], ref["group_expert_ids"])
+    check_gemm(y, o, written, f"mxfp4 split {split_k}")
+
+
+@pytest.mark.parametrize("case", sorted(BOUNDARY_CASES))
+def test_mxfp4_boundaries(case):
+    E, N, K, sizes, ids, M = BOUNDARY_CASES[case]
+    note(f"mxfp4 boundary {case}")
+    packed, scales = _stack(E, N, K, seed=31)
+    x = bf16_dev(np.random.default_rng(31).standard_normal((M, K)))
+    full = torch.full((M + 2, N), -512.0, dtype=torch.bfloat16, device=DEV)
+    y = full[1:M + 1]
+    st = torch.tensor(sizes, dtype=torch.int32, device=DEV)
+    it = torch.tensor(ids, dtype=torch.int32, device=DEV)
+    gnf4.grouped_gemm_mxfp4(x, packed, scales, st, it, G=len(sizes), y=y)
+    torch.cuda.synchronize()
+    o, written = _oracle(host_f64(x), packed, scales, sizes, ids)
+    f = full.float().cpu().numpy()
+    assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0), "guard rows written"
+    assert np.all(f[1:M + 1][~written] == -512.0), "uncovered rows written"
+    if written.any():
+        check_gemm(y, o, written, f"mxfp4 {case}")
+
+
+def test_mxfp4_scale_edges_and_nan():
+    """Expert 0 reads only blocks scaled 2^-127 (E8M0 0x00, a subnormal fp32)
+    and 2^-126 (0x01), against activations near 1e30; expert 1 has a block
+    scaled 2^127 (0xFE) against activations near 1e-30, and one NaN scale
+    (0xFF) that must poison exactly the outputs of its weight row."""
+    E, N, K, M = 2, 64, 256, 6
+    packed, _ = _stack(E, N, K, seed=41)
+    scales = torch.full((E, N, K // 32), 127, dtype=torch.uint8, device=DEV)
+    scales[0, :, 0] = 0
+    scales[0, :, 1] = 1
+    scales[1, :, 3] = 254
+    scales[1, 5, 2] = 255          # NaN block in weight row n = 5 of expert 1
+    rng = np.random.default_rng(41)
+    mag = rng.uniform(0.5, 1.5, (M, K)) * np.sign(rng.standard_normal((M, K)))
+    x = np.zeros((M, K), np.float32)
+    x[:3, :64] = (mag[:3, :64] * 1e30).astype(np.float32)     # expert 0: blocks 0 and 1 only
+    x[3:] = mag[3:].astype(np.float32)
+    x[3:, 96:128] = (mag[3:, 96:128] * 1e-30).astype(np.float32)
+    xd = bf16_dev(x)
+    sizes, ids = [3, 3], [0, 1]
+    note("mxfp4 scale edges")
+    y = gnf4.grouped_gemm_mxfp4(xd, packed, scales, torch.tensor(sizes, dtype=torch.int32,
+                                device=DEV), torch.tensor(ids, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    o, written = _oracle(host_f64(xd), packed, scales, sizes, ids)
+    g = host_f64(y)
+    nan_ref = np.isnan(o)
+    assert np.array_equal(np.isnan(g), nan_ref), "NaN positions differ"
+    assert nan_ref[3:, 5].all() and nan_ref.sum() == 3
+    for rows, what in ((slice(0, 3), "2^-127 / 2^-126 scales"), (slice(3, 6), "2^127 scale")):
+        ok = ~nan_ref[rows]
+        oo, gg = o[rows][ok], g[rows][ok]
+        rms = float(np.sqrt(np.mean(oo ** 2)))
+        assert rms > 0
+        bad = np.abs(gg - oo) > 8e-3 * np.abs(oo) + 1e-3 * rms
+        assert not bad.any(), f"{what}: {int(bad.sum())} outside tolerance"
+
+
+def test_mxfp4_gptoss_full_stack():
+    """GPT-OSS-120B-shaped gate_up: all 128 experts' MXFP4 bytes resident,
+    routed decode batch (T=1, k=4), every output checked."""
+    wl = wls.WORKLOADS["gptoss"]
+    K, N = wl.gemm("gate_up")
+    note(f"mxfp4 full stack gptoss gate_up E={wl.E} N={N} K={K}")
+    packed, scales = _stack(wl.E, N, K, seed=99, lo=115, hi=128)
+    logits = wls.router_logits(wl)
+    ref = oracle.ref_route_sort(logits, wl.top_k)
+    r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
+    x_tok = wls.token_activations(wl, K)
+    y = gnf4.grouped_gemm_mxfp4(bf16_dev(x_tok), packed, scales, r.group_sizes,
+                                r.group_expert_ids, sorted_slots=r.sorted_slots, top_k=wl.top_k)
+    torch.cuda.synchronize()
+    used = ref["group_expert_ids"][: ref["num_groups"]]
+    p = packed[torch.from_numpy(used.astype(np.int64)).to(DEV)].cpu().numpy()
+    s = scales[torch.from_numpy(used.astype(np.int64)).to(DEV)].cpu().numpy()
+    x_host = x_tok[ref["sorted_slots"] // wl.top_k]
+    ids_local = np.arange(len(used), dtype=np.int32)
+    o, written = oracle.ref_grouped_gemm_mxfp4(x_host, p, s, ref["group_sizes"][: len(used)],
+                                               ids_local)
+    check_gemm(y, o, written, "mxfp4 gptoss full stack")
