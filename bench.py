@@ -340,18 +340,22 @@ def time_dgrad(path, dev):
 
 def time_mxfp4(path, dev):
     """gnf4_grouped_gemm_mxfp4 alone at the decode shapes (GPT-OSS first: the
-    family released in MXFP4), cycling over enough random E2M1/E8M0 stack
-    copies to defeat the Infinity Cache; per-launch HIP events over a graph
-    of back-to-back launches with the fused gather.  Algorithmic bytes: each
-    touched expert's codes (N*K/2) and scales (N*K/32) once, the activation
-    rows read once, the output written once."""
+    family released in MXFP4) on the decode path, and at DeepSeek-V3's
+    prefill shapes on the automatic (tile) path, cycling over enough random
+    E2M1/E8M0 stack copies to defeat the Infinity Cache; per-launch HIP
+    events over a graph of back-to-back launches with the fused gather.
+    Algorithmic bytes: each touched expert's codes (N*K/2) and scales
+    (N*K/32) once, the activation rows read once, the output written once;
+    flops 2*M*N*K."""
     import torch
     from grouped_nf4_expert_amd import gnf4
     from grouped_nf4_expert_amd import workloads as wls
     out = open(path, "w")
     cells = (("gptoss", "gate_up"), ("gptoss", "down"), ("olmoe", "gate_up"), ("olmoe", "down"),
-             ("qwen3_t8", "gate_up"))
+             ("qwen3_t8", "gate_up"), ("dsv3", "gate_up"), ("dsv3", "down"))
     for name, gemm in cells:
+        prefill = name == "dsv3"
+        path_sel = gnf4.PATH_AUTO if prefill else gnf4.PATH_DECODE
         wl = wls.WORKLOADS[name]
         r = gnf4.route_sort(torch.from_numpy(wls.router_logits(wl)).to(dev), wl.top_k)
         G = min(wl.E, wl.M)
@@ -366,17 +370,18 @@ def time_mxfp4(path, dev):
                                  generator=gen)) for _ in range(copies)]
         x = wls.activations_device(wl.T, K, dev, wl.seed, 70, K)
         y = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(max(gnf4.gemm_workspace_size(wl.M, N, K, G, wl.E, gnf4.PATH_DECODE), 16),
+        ws = torch.empty(max(gnf4.gemm_workspace_size(wl.M, N, K, G, wl.E, path_sel), 16),
                          dtype=torch.uint8, device=dev)
-        per = 4 * copies
+        per = copies if prefill else 4 * copies
 
         def launches():
             for i in range(per):
                 p, sc = stacks[i % copies]
                 gnf4.grouped_gemm_mxfp4(x, p, sc, r.group_sizes, r.group_expert_ids, G=G, y=y,
-                                        workspace=ws, sorted_slots=r.sorted_slots, top_k=wl.top_k)
+                                        workspace=ws, path=path_sel, sorted_slots=r.sorted_slots,
+                                        top_k=wl.top_k)
         graph = capture(launches)
-        reps = 10
+        reps = 3 if prefill else 10
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
         graph.replay()
@@ -389,10 +394,15 @@ def time_mxfp4(path, dev):
         us = sorted(s_.elapsed_time(e_) * 1e3 / per for s_, e_ in evs)
         med = us[len(us) // 2]
         byt = ng * (N * K // 2 + N * K // 32) + 2 * wl.M * K + 2 * wl.M * N
-        rec = {"kernel": "mxfp4 grouped GEMM (decode path, fused gather)", "workload": name,
+        flops = 2.0 * wl.M * N * K
+        kind = "tile path" if prefill else "decode path"
+        rec = {"kernel": f"mxfp4 grouped GEMM ({kind}, fused gather)", "workload": name,
                "gemm": gemm, "M": wl.M, "N": N, "K": K, "touched_experts": ng,
                "median_us": round(med, 2), "GBps": round(byt / med / 1e3, 1),
-               "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4), "weight_copies": copies}
+               "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
+               "TFLOPs": round(flops / med / 1e6, 2),
+               "mfma_frac": round(flops / med / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4),
+               "weight_copies": copies}
         out.write(json.dumps(rec) + "\n")
         out.flush()
         print(f"[mxfp4] {json.dumps(rec)}", file=sys.stderr, flush=True)

@@ -330,15 +330,15 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
                                     int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                     const int32_t* group_expert_ids, int64_t G, int64_t M,
                                     uint16_t* y, void* workspace, size_t workspace_bytes,
-                                    int32_t split_k, void* stream) {
+                                    int32_t path, int32_t split_k, void* stream) {
   if (sorted_slots) {
     if (top_k < 1 || T < 0) return GNF4_ERR_INVALID_ARG;
     return gemm_common(x, packed, scales, kScaleE8M0, E, N, K, group_sizes, group_expert_ids, G,
-                       M, y, workspace, workspace_bytes, 1, split_k, stream, sorted_slots, top_k,
-                       T);
+                       M, y, workspace, workspace_bytes, path, split_k, stream, sorted_slots,
+                       top_k, T);
   }
   return gemm_common(x, packed, scales, kScaleE8M0, E, N, K, group_sizes, group_expert_ids, G, M,
-                     y, workspace, workspace_bytes, 1, split_k, stream);
+                     y, workspace, workspace_bytes, path, split_k, stream);
 }
 
 gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,

@@ -121,10 +121,11 @@ __device__ __forceinline__ half8 decode8(uint32_t d, const Table& t) {
 }
 
 // 8 bf16 (natural K order), times 2^t when SCALED, -> 8 fp16 in the
-// decode's slot order.  The row's exponent keeps every value below 2^15, and
-// bf16 values in the fp16 normal range convert exactly, so round-toward-zero
-// packing is exact.
-template <bool SCALED>
+// decode's slot order (NATURAL: K order, for MXFP4 whose convert yields the
+// low-nibble element first).  The row's exponent keeps every value below
+// 2^15, and bf16 values in the fp16 normal range convert exactly, so
+// round-toward-zero packing is exact.
+template <bool SCALED, bool NATURAL = false>
 __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v, int t) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
   float f[8];
@@ -138,10 +139,38 @@ __device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v, int t) {
     }
   }
   uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[2]));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[6]));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[1], f[3]));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[5], f[7]));
+  if constexpr (NATURAL) {
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3]));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[5]));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[6], f[7]));
+  } else {
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[2]));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[6]));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[1], f[3]));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[5], f[7]));
+  }
+  return r;
+}
+
+// The stack's scale type names its format: fp32 or bf16 block absmax (NF4),
+// or uint8 E8M0 scales (MXFP4: E2M1 codes, one scale per 32, low nibble
+// first).
+template <typename AbsT>
+constexpr bool kTileMx = std::is_same_v<AbsT, uint8_t>;
+
+// MXFP4: the 8 codes of dword d -> MFMA operand in K order.  gfx950's
+// convert applies the exponent of `scale` exactly (E8M0 scales are powers of
+// two): `scale` carries the block scale times the weight row's 2^-s_n.
+__device__ __forceinline__ half8 mx_decode8(uint32_t d, float scale) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 0);
+  const h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 1);
+  const h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 2);
+  const h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 3);
+  half8 r;
+  r[0] = p0.x; r[1] = p0.y; r[2] = p1.x; r[3] = p1.y;
+  r[4] = p2.x; r[5] = p2.y; r[6] = p3.x; r[7] = p3.y;
   return r;
 }
 
@@ -154,6 +183,7 @@ struct PassCtx {
   const void* arow;        // its absmax row (fp32, or bf16 bits)
   bool n_ok;               // the lane's column exists
   int sexp;                // its power-of-two scale exponent
+  bool col_nan;            // MXFP4: the weight row holds a NaN scale
   int tid, i, h, N, K, bpr, n, p0, rows, r_end, n_steps, rem_k;
 };
 
@@ -229,7 +259,8 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
       const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
       const uint4 v = ok ? xr[sl][j] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&c.s_x[buf * (kPassRows * kLdsRow) + row * kLdsRow + 8 * c16]) =
-          scaled ? bf16x8_to_f16_slots<true>(v, c.s_exp[row]) : bf16x8_to_f16_slots<false>(v, 0);
+          scaled ? bf16x8_to_f16_slots<true, kTileMx<AbsT>>(v, c.s_exp[row])
+                 : bf16x8_to_f16_slots<false, kTileMx<AbsT>>(v, 0);
     }
   };
   // weight codes: the lane's 32 bytes of block h of the step, and its absmax
@@ -240,7 +271,14 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
     const uint4* p = reinterpret_cast<const uint4*>(c.wrow + (ok ? 32 * (size_t)blk : 0));
     wc[sl][0] = p[0];
     wc[sl][1] = p[1];
-    wa[sl] = absmax_at(static_cast<const AbsT*>(c.arow), ok ? blk : 0);
+    if constexpr (kTileMx<AbsT>) {
+      // the two E8M0 scales of the 64-code block, packed in a register
+      const uint8_t* ar = static_cast<const uint8_t*>(c.arow);
+      const uint32_t s0 = ar[ok ? 2 * blk : 0], s1 = ar[ok ? 2 * blk + 1 : 1];
+      wa[sl] = __uint_as_float(s0 | (s1 << 8));
+    } else {
+      wa[sl] = absmax_at(static_cast<const AbsT*>(c.arow), ok ? blk : 0);
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -254,11 +292,25 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
     const bool cok = c.n_ok && 2 * step + c.h < c.bpr;
     load_x(slot_c, min(step + 2, last));
     load_w(slot_c, min(step + 2, last));
-    const Table tab = make_table(cok ? ldexpf(ca, -c.sexp) : 0.0f);
+    Table tab;
+    float sc0 = 0.0f, sc1 = 0.0f;
+    if constexpr (kTileMx<AbsT>) {
+      // an absent block converts with scale 0, which the convert treats as
+      // 2^-127: its values vanish in fp16
+      const uint32_t sb = __float_as_uint(ca);
+      sc0 = cok ? ldexpf(1.0f, (int)(sb & 0xffu) - 127 - c.sexp) : 0.0f;
+      sc1 = cok ? ldexpf(1.0f, (int)((sb >> 8) & 0xffu) - 127 - c.sexp) : 0.0f;
+    } else {
+      tab = make_table(cok ? ldexpf(ca, -c.sexp) : 0.0f);
+    }
     const _Float16* xs = c.s_x + sl * (kPassRows * kLdsRow);
 #pragma unroll
     for (int sub = 0; sub < 8; ++sub) {
-      const half8 bw = decode8((&cw[0].x)[sub], tab);
+      half8 bw;
+      if constexpr (kTileMx<AbsT>)
+        bw = mx_decode8((&cw[0].x)[sub], sub < 4 ? sc0 : sc1);
+      else
+        bw = decode8((&cw[0].x)[sub], tab);
       half8 ax[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -306,7 +358,10 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
     for (int v = 0; v < 16; ++v) {
       const int row = c.p0 + rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
       if (row >= c.r_end || ((skip >> v) & 1u)) continue;
-      g.y[(size_t)row * c.N + c.n] = f32_to_bf16(ldexpf(acc[rt][v], c.sexp - c.s_exp[row - c.p0]));
+      uint16_t out = f32_to_bf16(ldexpf(acc[rt][v], c.sexp - c.s_exp[row - c.p0]));
+      if constexpr (kTileMx<AbsT>)
+        if (c.col_nan) out = 0x7fc0u;  // a NaN scale reaches every output of the row
+      g.y[(size_t)row * c.N + c.n] = out;
     }
   }
 }
@@ -339,7 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
   const uint8_t* wexp = a.g.packed + (size_t)e * N * row_bytes;
-  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)e * N * bpr;
+  const int spr = kTileMx<AbsT> ? 2 * bpr : bpr;  // scales per weight row
+  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)e * N * spr;
 
   // activation exponent of output row `row` (by token when the gather is
   // fused and the exponents were taken per token); the first pass's are
@@ -357,35 +413,60 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const bool n_ok = n < N;
   // (16 independent loads per round: an index past the row re-reads a block
   // of the same row, which leaves the maximum unchanged)
-  float m = 0.0f;
-  {
-    const AbsT* ar = aexp + (n_ok ? (size_t)n * bpr : 0);
-    float mu[16];
+  int sexp = 0;
+  bool col_nan = false;
+  if constexpr (kTileMx<AbsT>) {
+    // MXFP4: the row's largest E8M0 scale s_max; 2^-s_n = 2^-(s_max - 127)
+    // puts every decoded value at or below 6 (fp16-safe)
+    const uint8_t* ar = aexp + (n_ok ? (size_t)n * spr : 0);
+    uint32_t mu[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) mu[u] = 0.0f;
-    for (int bk0 = h; bk0 < bpr; bk0 += 32) {
+    for (int u = 0; u < 16; ++u) mu[u] = 0u;
+    for (int b0 = h; b0 < spr; b0 += 32) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int bk = bk0 + 2 * u;
-        mu[u] = fmaxf(mu[u], absmax_at(ar, bk < bpr ? bk : h));
+        const int b = b0 + 2 * u;
+        mu[u] = max(mu[u], (uint32_t)ar[b < spr ? b : h]);
       }
     }
+    uint32_t mx = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) m = fmaxf(m, mu[u]);
-    if (!n_ok) m = 0.0f;
+    for (int u = 0; u < 16; ++u) mx = max(mx, mu[u]);
+    if (!n_ok) mx = 0;
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, kWave));
+    sexp = (int)mx - 127;
+    col_nan = mx == 255u;
+  } else {
+    float m = 0.0f;
+    {
+      const AbsT* ar = aexp + (n_ok ? (size_t)n * bpr : 0);
+      float mu[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mu[u] = 0.0f;
+      for (int bk0 = h; bk0 < bpr; bk0 += 32) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int bk = bk0 + 2 * u;
+          mu[u] = fmaxf(mu[u], absmax_at(ar, bk < bpr ? bk : h));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m = fmaxf(m, mu[u]);
+      if (!n_ok) m = 0.0f;
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    (void)frexpf(m, &sexp);
   }
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  int sexp = 0;
-  (void)frexpf(m, &sexp);
 
   PassCtx c;
   c.a = &a;
   c.s_x = &s_x[0][0];
   c.s_exp = s_exp;
   c.wrow = wexp + (n_ok ? (size_t)n * row_bytes : 0);
-  c.arow = aexp + (n_ok ? (size_t)n * bpr : 0);
+  c.arow = aexp + (n_ok ? (size_t)n * spr : 0);
   c.n_ok = n_ok;
   c.sexp = sexp;
+  c.col_nan = col_nan;
   c.tid = tid;
   c.i = i;
   c.h = h;
@@ -493,7 +574,9 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   a.n_work = (int)group_slots(g.G, g.M, g.rows_min_tile) * a.n_tiles;
   const int grid = ((a.n_work + 7) / 8) * 8;
   if (grid == 0) return hipSuccess;
-  if (g.abs_bf16)
+  if (g.mxfp4)
+    hipLaunchKernelGGL(tile_kernel<uint8_t>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (g.abs_bf16)
     hipLaunchKernelGGL(tile_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(tile_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);

@@ -69,7 +69,7 @@ def library():
                                        i32, vp]
     lib.gnf4_grouped_gemm_mxfp4.restype = ctypes.c_int
     lib.gnf4_grouped_gemm_mxfp4.argtypes = [vp, i64, vp, i32, vp, vp, i64, i64, i64, vp, vp, i64,
-                                            i64, vp, vp, sz, i32, vp]
+                                            i64, vp, vp, sz, i32, i32, vp]
     lib.gnf4_swiglu.restype = ctypes.c_int
     lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
     lib.gnf4_combine.restype = ctypes.c_int
@@ -205,10 +205,11 @@ def route_sort(logits, top_k, buffers=None):
 # ------------------------------------------------------------------ MXFP4
 
 def grouped_gemm_mxfp4(x, packed, scales, group_sizes, group_expert_ids, G=None, y=None,
-                       workspace=None, split_k=0, sorted_slots=None, top_k=1):
+                       workspace=None, path=PATH_AUTO, split_k=0, sorted_slots=None, top_k=1):
     """y[M, N] (bf16) over an MXFP4 stack: ``packed`` [E, N, K/2] uint8 E2M1
     codes (element 2j in the low nibble), ``scales`` [E, N, K/32] uint8 E8M0.
-    With ``sorted_slots`` the gather is fused as in grouped_gemm."""
+    With ``sorted_slots`` the gather is fused, and ``path`` picks the kernels,
+    as in grouped_gemm."""
     _need(x, "x", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 3)
     _need(scales, "scales", torch.uint8, 3)
@@ -225,14 +226,14 @@ def grouped_gemm_mxfp4(x, packed, scales, group_sizes, group_expert_ids, G=None,
         G = min(group_sizes.numel(), M)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    need = gemm_workspace_size(M, N, K, G, E, PATH_DECODE, split_k)
+    need = gemm_workspace_size(M, N, K, G, E, path, split_k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(library().gnf4_grouped_gemm_mxfp4(
         _ptr(x), rows, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(scales), E, N, K,
         _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
-        split_k, _stream()), "gnf4_grouped_gemm_mxfp4")
+        path, split_k, _stream()), "gnf4_grouped_gemm_mxfp4")
     return y
 
 

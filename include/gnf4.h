@@ -183,14 +183,19 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
  *   packed        [E, N, K/2] uint8: E2M1 codes, element 2j in the LOW nibble
  *                 of byte j (16-byte aligned)
  *   scales        [E, N, K/32] uint8 E8M0: scale 2^(s - 127); 0xFF is NaN
- *   other arguments as in gnf4_grouped_gemm_gather / gnf4_grouped_gemm_ex;
- *   workspace     gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, 1, split_k)
+ *   other arguments as in gnf4_grouped_gemm_gather / gnf4_grouped_gemm_ex,
+ *   `path` included (0 auto: groups of up to 8 rows on the decode path, the
+ *   rest on the matrix-core tile path);
+ *   workspace     gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, path,
+ *                 split_k)
  *
- * Codes are decoded by gfx950's E2M1 convert and each 32-code partial sum,
- * accumulated in fp32, is multiplied by its block scale; bf16 output within
- * the GEMM's tolerance.  All groups run on the decode path (there is no
- * matrix-core MXFP4 path yet), so it suits decode-sized groups; large groups
- * are correct but re-read each expert's codes once per 4 rows.
+ * Codes are decoded by gfx950's E2M1 convert.  Decode path: each 32-code
+ * partial sum, accumulated in fp32, is multiplied by its block scale.  Tile
+ * path: codes convert to fp16 scaled by 2^(s - s_max), s_max the largest
+ * scale of the weight row (exact: powers of two), activations as in the NF4
+ * tile path, fp32 MFMA accumulation, 2^(s_max - 127) applied at the end; a
+ * weight row with a NaN scale gives NaN in every output of that column.
+ * bf16 output within the GEMM's tolerance.
  * Limits and errors: as gnf4_grouped_gemm_gather (K % 64 == 0).
  */
 gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t* sorted_slots,
@@ -198,7 +203,7 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
                                     int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
                                     const int32_t* group_expert_ids, int64_t G, int64_t M,
                                     uint16_t* y, void* workspace, size_t workspace_bytes,
-                                    int32_t split_k, void* stream);
+                                    int32_t path, int32_t split_k, void* stream);
 
 /*
  * gnf4_grouped_dgrad -- the activation gradient of the grouped GEMM over the
