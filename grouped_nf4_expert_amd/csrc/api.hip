@@ -21,6 +21,17 @@ gnf4_status hip_fail(hipError_t e) {
 // MFMA rows would be mostly padding, above it the fp32 decode path's
 // per-row multiply-adds cost more than the matrix core.
 constexpr int kDecodeMaxRows = 8;
+// A batch averaging at least this many rows per group (prefill) puts every
+// group on the tile path: a decode launch there only has its workgroups
+// scan the group list for the rare small group, which costs more than the
+// tile kernel spends on such a group.
+constexpr int64_t kTileOnlyRowsPerGroup = 32;
+
+// The automatic path choice, from host-known sizes only.
+static bool auto_tile_only(int64_t M, int64_t G) {
+  const int64_t g_eff = G < M ? G : M;
+  return g_eff > 0 && M >= kTileOnlyRowsPerGroup * g_eff;
+}
 
 bool is_device_ptr(const void* p) {
   if (p == nullptr) return false;
@@ -210,6 +221,10 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
     a.rows_max_decode = 0;
     a.rows_min_tile = 1;
     run_decode = false;
+  } else if (auto_tile_only(M, G)) {
+    a.rows_max_decode = 0;
+    a.rows_min_tile = 1;
+    run_decode = false;
   } else {
     a.rows_max_decode = kDecodeMaxRows;
     a.rows_min_tile = kDecodeMaxRows + 1;
@@ -387,9 +402,10 @@ size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int6
                                            int64_t E, int32_t path, int32_t split_k) {
   (void)E;
   if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
-  const bool tile = path == 2 || (path == 0 && M > kDecodeMaxRows);
+  const bool tile_only = path == 2 || (path == 0 && auto_tile_only(M, G));
+  const bool tile = tile_only || (path == 0 && M > kDecodeMaxRows);
   const size_t tile_bytes = tile ? row_exp_bytes(M) : 0;
-  if (path == 2) return tile_bytes;
+  if (tile_only) return tile_bytes;
   const DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
   return tile_bytes + decode_workspace_bytes(p, M, N);
 }

@@ -322,7 +322,10 @@ gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const floa
  * fp16 -> fp32 MFMA).  Which one runs is a performance choice made from
  * host-known sizes only; both meet |y - exact| <= 8e-3 |exact| +
  * 1e-3 rms(exact) per element for any finite bf16 activations.  Results are
- * deterministic run to run.
+ * deterministic run to run.  The automatic choice: groups of up to 8 rows
+ * take the decode path and larger ones the tile path, except that a batch
+ * averaging at least 32 rows per group (M >= 32 min(G, M), prefill) runs
+ * every group on the tile path and launches no decode kernel.
  *
  * Limits: M >= 0, G >= 0 (either 0: nothing to do), E, N >= 1, K >= 64 with
  * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call,

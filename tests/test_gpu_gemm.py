@@ -127,6 +127,9 @@ BOUNDARY_CASES = {
                            list(range(300)), 17),
     # more non-empty groups than rows: the later groups start past M
     "groups_beyond_M": (12, 64, 128, [1] * 12, list(range(12)), 8),
+    # a prefill-sized batch (at least 32 rows per group on average) holding
+    # groups of 1, 2 and 8 rows: the automatic path runs all on the tile path
+    "prefill_small_groups": (5, 96, 256, [1, 8, 150, 2, 60], [4, 0, 3, 1, 2], 221),
 }
 
 
