@@ -76,6 +76,8 @@ def parse():
                     help="time the SwiGLU and top-k combine kernels alone into this JSONL")
     ap.add_argument("--absmax-dtype", choices=("f32", "bf16"), default="f32",
                     help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workload names: restrict --cells / --mxfp4 / --dgrad to them")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -208,7 +210,7 @@ def cpu_baseline(wl, seconds):
                       f"{n} touched experts) in {el:.1f} s; fp64 numpy, BLAS threads={threads}"}
 
 
-def time_cells(path, dev):
+def time_cells(path, dev, only=()):
     """Each workload's GEMMs alone, cycling over enough weight copies to
     defeat the Infinity Cache; per-launch HIP events."""
     import torch
@@ -216,6 +218,8 @@ def time_cells(path, dev):
     from grouped_nf4_expert_amd import workloads as wls
     out = open(path, "w")
     for name in ("olmoe", "qwen3_t1", "qwen3_t8", "gptoss", "dsv3"):
+        if only and name not in only:
+            continue
         wl = wls.WORKLOADS[name]
         lg = torch.from_numpy(wls.router_logits(wl)).to(dev)
         r = gnf4.route_sort(lg, wl.top_k)
@@ -273,7 +277,7 @@ def time_cells(path, dev):
     out.close()
 
 
-def time_dgrad(path, dev):
+def time_dgrad(path, dev, only=()):
     """gnf4_grouped_dgrad alone, cycling over enough weight copies to defeat
     the Infinity Cache (as the forward cells); per-launch HIP events over a
     graph of back-to-back launches.  Algorithmic bytes as the forward GEMM
@@ -285,6 +289,8 @@ def time_dgrad(path, dev):
     cells = (("olmoe", "gate_up"), ("olmoe", "down"), ("qwen3_t8", "gate_up"),
              ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"))
     for name, gemm in cells:
+        if only and name not in only:
+            continue
         wl = wls.WORKLOADS[name]
         lg = torch.from_numpy(wls.router_logits(wl)).to(dev)
         r = gnf4.route_sort(lg, wl.top_k)
@@ -338,7 +344,7 @@ def time_dgrad(path, dev):
     out.close()
 
 
-def time_mxfp4(path, dev):
+def time_mxfp4(path, dev, only=()):
     """gnf4_grouped_gemm_mxfp4 alone at the decode shapes (GPT-OSS first: the
     family released in MXFP4) on the decode path, and at DeepSeek-V3's
     prefill shapes on the automatic (tile) path, cycling over enough random
@@ -354,6 +360,8 @@ def time_mxfp4(path, dev):
     cells = (("gptoss", "gate_up"), ("gptoss", "down"), ("olmoe", "gate_up"), ("olmoe", "down"),
              ("qwen3_t8", "gate_up"), ("dsv3", "gate_up"), ("dsv3", "down"))
     for name, gemm in cells:
+        if only and name not in only:
+            continue
         prefill = name == "dsv3"
         path_sel = gnf4.PATH_AUTO if prefill else gnf4.PATH_DECODE
         wl = wls.WORKLOADS[name]
@@ -554,14 +562,18 @@ def main():
     gnf4.library()
     dev = torch.device("cuda:0")
 
+    only = tuple(w for w in args.only.split(",") if w)
     if args.glue:
         time_glue(args.glue, dev)
         return
+    if args.cells and only:  # the named workloads' GEMM cells alone, no step
+        time_cells(args.cells, dev, only)
+        return
     if args.dgrad:
-        time_dgrad(args.dgrad, dev)
+        time_dgrad(args.dgrad, dev, only)
         return
     if args.mxfp4:
-        time_mxfp4(args.mxfp4, dev)
+        time_mxfp4(args.mxfp4, dev, only)
         return
 
     if args.copy_mb:
@@ -710,7 +722,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
     if args.cells:
-        time_cells(args.cells, dev)
+        time_cells(args.cells, dev, only)
 
 
 if __name__ == "__main__":
