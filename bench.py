@@ -287,7 +287,7 @@ def time_dgrad(path, dev, only=()):
     from grouped_nf4_expert_amd import workloads as wls
     out = open(path, "w")
     cells = (("olmoe", "gate_up"), ("olmoe", "down"), ("qwen3_t8", "gate_up"),
-             ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"))
+             ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"), ("dsv3", "gate_up"))
     for name, gemm in cells:
         if only and name not in only:
             continue
@@ -332,10 +332,13 @@ def time_dgrad(path, dev, only=()):
         med = us[len(us) // 2]
         byt = gemm_bytes(ng, wl.M, N, K)
         flops = 2.0 * wl.M * N * K
-        rec = {"kernel": "dgrad", "workload": name, "gemm": gemm, "M": wl.M, "N": N, "K": K,
+        kind = "tile path" if wl.M >= 32 * G else "GEMV path"  # the automatic choice
+        rec = {"kernel": f"dgrad ({kind})", "workload": name, "gemm": gemm, "M": wl.M, "N": N, "K": K,
                "touched_experts": ng, "median_us": round(med, 2), "GBps": round(byt / med / 1e3, 1),
                "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
-               "TFLOPs": round(flops / med / 1e6, 2), "weight_copies": copies}
+               "TFLOPs": round(flops / med / 1e6, 2),
+               "mfma_frac": round(flops / med / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4),
+               "weight_copies": copies}
         out.write(json.dumps(rec) + "\n")
         out.flush()
         print(f"[dgrad] {json.dumps(rec)}", file=sys.stderr, flush=True)

@@ -4,6 +4,7 @@
 #include <limits.h>
 #include <string.h>
 
+#include "dgrad_tile.h"
 #include "gnf4_internal.h"
 
 namespace gnf4 {
@@ -282,20 +283,38 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
-size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G,
-                                         int64_t E) {
+// The dgrad's matrix-core path reads dy in 16-byte chunks.
+static bool dgrad_tile_ok(const uint16_t* dy, int64_t N) { return N % 8 == 0 && aligned(dy, 16); }
+
+// Path of a dgrad call: 2 = tile, 1 = GEMV.  Automatic: a batch averaging
+// at least 32 rows per group (prefill) takes the tile path when dy's layout
+// allows it; the GEMV path re-reads the weights once per 4 rows of dy.
+static int dgrad_path(int32_t path, int64_t M, int64_t G, bool tile_ok) {
+  if (path == 0) return auto_tile_only(M, G) && tile_ok ? 2 : 1;
+  return path;
+}
+
+size_t gnf4_grouped_dgrad_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
+                                            int64_t E, int32_t path) {
   (void)E;
   if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
+  if (dgrad_path(path, M, G, N % 8 == 0) == 2) return row_exp_bytes(M);
   return dgrad_workspace_bytes(plan_dgrad(M, N, K, G, device_cu_count()), M, K);
 }
 
-gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const void* absmax,
-                               int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
-                               const int32_t* group_expert_ids, int64_t G, int64_t M,
-                               uint16_t* dx, void* workspace, size_t workspace_bytes,
-                               int32_t absmax_dtype, void* stream) {
+size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G,
+                                         int64_t E) {
+  return gnf4_grouped_dgrad_workspace_size_ex(M, N, K, G, E, 0);
+}
+
+gnf4_status gnf4_grouped_dgrad_ex(const uint16_t* dy, const uint8_t* packed, const void* absmax,
+                                  int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                  const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                  uint16_t* dx, void* workspace, size_t workspace_bytes,
+                                  int32_t absmax_dtype, int32_t path, void* stream) {
   if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
     return GNF4_ERR_INVALID_ARG;
+  if (path < 0 || path > 2) return GNF4_ERR_INVALID_ARG;
   if (M == 0 || G == 0) return GNF4_OK;
   if (N * (K / 2) >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31) ||
       M * N >= ((int64_t)1 << 31) || E * N >= ((int64_t)1 << 31) || G >= 65536)
@@ -324,6 +343,27 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
   a.K = (int)K;
   a.G = (int)G;
   a.M = (int)M;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool tile_ok = dgrad_tile_ok(dy, N);
+  const int run = dgrad_path(path, M, G, tile_ok);
+  if (run == 2) {
+    if (!tile_ok) return GNF4_ERR_UNSUPPORTED;  // forced tile path, dy not in 16-byte chunks
+    if (!workspace || workspace_bytes < row_exp_bytes(M)) return GNF4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return GNF4_ERR_INVALID_ARG;
+    if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
+    // per-row exponents of dy, by the forward's pre-pass over an [M, N] matrix
+    GemmArgs g{};
+    g.x = dy;
+    g.slots = nullptr;
+    g.slot_div = 1;
+    g.T = 0;
+    g.M = (int)M;
+    g.K = (int)N;
+    g.row_exp = static_cast<int32_t*>(workspace);
+    hipError_t e = launch_row_exp(g, s);
+    if (e == hipSuccess) e = launch_dgrad_tile(a, g.row_exp, 1, s);
+    return e == hipSuccess ? GNF4_OK : hip_fail(e);
+  }
   DgradPlan p = plan_dgrad(M, N, K, G, device_cu_count());
   const size_t need = dgrad_workspace_bytes(p, M, K);
   if (need > 0) {
@@ -336,8 +376,17 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
       a.partial = static_cast<float*>(workspace);
     }
   }
-  const hipError_t e = launch_dgrad(a, p, (hipStream_t)stream);
+  const hipError_t e = launch_dgrad(a, p, s);
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const void* absmax,
+                               int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                               const int32_t* group_expert_ids, int64_t G, int64_t M,
+                               uint16_t* dx, void* workspace, size_t workspace_bytes,
+                               int32_t absmax_dtype, void* stream) {
+  return gnf4_grouped_dgrad_ex(dy, packed, absmax, E, N, K, group_sizes, group_expert_ids, G, M,
+                               dx, workspace, workspace_bytes, absmax_dtype, 0, stream);
 }
 
 gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t* sorted_slots,

@@ -42,6 +42,7 @@
 
 #include <type_traits>
 
+#include "dgrad_tile.h"
 #include "gnf4_internal.h"
 
 namespace gnf4 {
@@ -500,6 +501,254 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ dgrad
+// Matrix-core dgrad, dx[r, k] = sum_n dy[r, n] W[n, k] per group (page
+// "grouped-nf4-gemm", "Owns": the grouped packed GEMM and its dgrad).  The
+// contraction runs over N, across the rows of each expert's K-contiguous
+// codes, so the decoded weights are written to LDS transposed, [k][n], and
+// read back as MFMA operands of 8 consecutive n.  A workgroup of 4
+// wavefronts owns (group, 128 columns of K) and walks N in steps of 64; each
+// wavefront owns 32 of the columns for every row of the group (up to 4 row
+// tiles of 32 per pass), so each code is decoded once per pass.
+//  * weights: lane l of wavefront w loads the 16 bytes (32 codes, one
+//    64-code absmax block) at row n0 + l, columns k0 + 32 w, and decodes them
+//    through the fp16 table of fp16(level * absmax * 2^-S), one rounding,
+//    where 2^-S puts the largest block absmax of that 64-column block over
+//    all N rows into [0.5, 1) (the contraction mixes rows, so the scale is
+//    per output column, applied exactly in the epilogue);
+//  * dy: the pass's rows x 64 n staged as fp16 times each row's 2^t_r, as
+//    the forward stages activations (t_r from the row-exponent pre-pass over
+//    dy);
+//  * fp32 accumulation on v_mfma_f32_32x32x16_f16, dx = acc * 2^(S - t_r)
+//    rounded once to bf16.
+// A block whose absmax lies 2^24 or more below its column block's largest
+// flushes toward zero in fp16, the range limit of the forward tile path
+// with the roles of rows and columns exchanged.
+constexpr int kDgThreads = 256;    // 4 wavefronts, 32 output columns each
+constexpr int kDgTileK = 128;      // output columns (of K) per workgroup
+constexpr int kDgStepN = 64;       // rows of W (contraction) per step
+constexpr int kDgRowTiles = 4;     // 32-row MFMA tiles per pass
+constexpr int kDgPassRows = 32 * kDgRowTiles;
+constexpr int kDgLds = kDgStepN + 8;  // fp16 per LDS row: 144 bytes, conflict-free reads
+
+struct DgradTileKArgs {
+  DgradArgs d;
+  const int32_t* row_exp;
+  int rows_min;
+  int k_tiles;
+  int n_work;  // group slots * k_tiles
+};
+
+struct DgPassCtx {
+  const DgradTileKArgs* a;
+  _Float16* s_w;   // [2][kDgTileK * kDgLds], [k][n]
+  _Float16* s_dy;  // [2][kDgPassRows * kDgLds], [row][n]
+  const int* s_exp;
+  const uint8_t* wexp;
+  const void* aexp;
+  int sexp;        // this wavefront's column-block exponent S
+  int tid, wave, lane, i, h, N, K, bpr, k0, p0, rows;
+};
+
+template <int RT, typename AbsT>
+__device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
+  const DgradArgs& d = c.a->d;
+  float16v acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[rt][v] = 0.0f;
+
+  const int steps = (c.N + kDgStepN - 1) / kDgStepN;
+  const size_t row_bytes = (size_t)c.K / 2;
+  const int kk = c.k0 + 32 * c.wave;  // this wavefront's first code column
+  const bool k_ok = kk < c.K;
+  uint4 wr;
+  float war;
+  uint4 yr[RT];
+  // Loads of step s are issued at the top of step s - 1 and consumed (staged
+  // into LDS) at its end, so no loaded register lives across the loop's
+  // back edge.
+  auto load = [&](int step) {
+    const int n = step * kDgStepN + c.lane;
+    const bool ok = k_ok && n < c.N;
+    wr = *reinterpret_cast<const uint4*>(c.wexp + (ok ? (size_t)n * row_bytes + kk / 2 : 0));
+    war = absmax_at(static_cast<const AbsT*>(c.aexp) + (ok ? (size_t)n * c.bpr : 0),
+                    ok ? kk / kBlock : 0);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const int q = c.tid + kDgThreads * j;
+      const int row = q >> 3, nn = step * kDgStepN + 8 * (q & 7);
+      const bool okr = row < c.rows && nn < c.N;
+      yr[j] = *reinterpret_cast<const uint4*>(d.dy + (okr ? (size_t)(c.p0 + row) * c.N + nn : 0));
+    }
+  };
+  auto stage = [&](int buf, int step) {
+    const int n = step * kDgStepN + c.lane;
+    const bool ok = k_ok && n < c.N;
+    const Table tab = make_table(ok ? ldexpf(war, -c.sexp) : 0.0f);
+    _Float16* sw = c.s_w + buf * (kDgTileK * kDgLds) + c.lane;
+    const uint32_t dw[4] = {wr.x, wr.y, wr.z, wr.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // slot order of decode8: codes {0, 2, 4, 6, 1, 3, 5, 7} of the dword
+      const half8 v = decode8(dw[q], tab);
+      const int kc = 32 * c.wave + 8 * q;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kcode = e < 4 ? 2 * e : 2 * (e - 4) + 1;
+        sw[(kc + kcode) * kDgLds] = v[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const int q = c.tid + kDgThreads * j;
+      const int row = q >> 3, c8 = q & 7;
+      const int nn = step * kDgStepN + 8 * c8;
+      const bool okr = row < c.rows && nn < c.N;
+      const uint4 v = okr ? yr[j] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&c.s_dy[buf * (kDgPassRows * kDgLds) + row * kDgLds + 8 * c8]) =
+          scaled ? bf16x8_to_f16_slots<true, true>(v, c.s_exp[row])
+                 : bf16x8_to_f16_slots<false, true>(v, 0);
+    }
+  };
+
+  load(0);
+  stage(0, 0);
+  __syncthreads();
+  for (int step = 0; step < steps; ++step) {
+    const int buf = step & 1;
+    const bool more = step + 1 < steps;
+    if (more) load(step + 1);
+    const _Float16* sw = c.s_w + buf * (kDgTileK * kDgLds) + (32 * c.wave + c.i) * kDgLds + 8 * c.h;
+    const _Float16* sy = c.s_dy + buf * (kDgPassRows * kDgLds) + c.i * kDgLds + 8 * c.h;
+#pragma unroll
+    for (int sub = 0; sub < kDgStepN / 16; ++sub) {
+      const half8 bw = *reinterpret_cast<const half8*>(sw + 16 * sub);
+      half8 ax[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        ax[rt] = *reinterpret_cast<const half8*>(sy + rt * 32 * kDgLds + 16 * sub);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[rt], bw, acc[rt], 0, 0, 0);
+    }
+    if (more) stage(1 - buf, step + 1);
+    __syncthreads();
+  }
+
+  // epilogue: D[row][col], col = lane % 32, row = 8 (v / 4) + 4 h + v % 4
+  const int k = kk + c.i;
+  if (!k_ok || k >= c.K) return;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
+      if (row >= c.rows) continue;
+      d.dx[(size_t)(c.p0 + row) * c.K + k] =
+          f32_to_bf16(ldexpf(acc[rt][v], c.sexp - c.s_exp[row]));
+    }
+}
+
+template <typename AbsT>
+__global__ __launch_bounds__(kDgThreads, 2) void dgrad_tile_kernel(DgradTileKArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_w[2 * kDgTileK * kDgLds];
+  __shared__ __attribute__((aligned(16))) _Float16 s_dy[2 * kDgPassRows * kDgLds];
+  __shared__ int s_exp[kDgPassRows];
+  __shared__ float s_max[2][kDgThreads / kWave];
+
+  // XCD-aware order: consecutive work items land on one XCD.
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int work = (b & 7) * (nb >> 3) + (b >> 3);
+  if (work >= a.n_work) return;
+  const int kt = work % a.k_tiles;
+  GroupRef gr;
+  if (!find_group(a.d.sizes, a.d.ids, a.d.G, a.d.E, a.d.M, a.rows_min, INT_MAX, work / a.k_tiles,
+                  gr))
+    return;
+  const int e = gr.expert;
+  const int r_begin = gr.row;
+  const int r_end = min(r_begin + gr.size, a.d.M);
+  if (r_begin >= r_end) return;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int N = a.d.N, K = a.d.K, bpr = K / kBlock;
+  const int k0 = kt * kDgTileK;
+  const int kb0 = k0 / kBlock;  // the tile's two absmax blocks: kb0, kb0 + 1
+  const bool has_b1 = kb0 + 1 < bpr;
+  const AbsT* aexp = static_cast<const AbsT*>(a.d.absmax) + (size_t)e * N * bpr;
+
+  // column-block scales: the largest absmax of blocks kb0 and kb0 + 1 over
+  // all N rows (4 independent loads per round per thread)
+  float m0 = 0.0f, m1 = 0.0f;
+  for (int n0 = tid; n0 < N; n0 += 4 * kDgThreads) {
+    float v0[4], v1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + u * kDgThreads;
+      const AbsT* ar = aexp + (size_t)(n < N ? n : n0) * bpr;
+      v0[u] = absmax_at(ar, kb0);
+      v1[u] = absmax_at(ar, has_b1 ? kb0 + 1 : kb0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m0 = fmaxf(m0, v0[u]);
+      m1 = fmaxf(m1, v1[u]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, o, kWave));
+    m1 = fmaxf(m1, __shfl_xor(m1, o, kWave));
+  }
+  if (lane == 0) {
+    s_max[0][wave] = m0;
+    s_max[1][wave] = m1;
+  }
+  __syncthreads();
+  // wavefronts 0, 1 own the columns of block kb0, wavefronts 2, 3 those of kb0 + 1
+  float m = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDgThreads / kWave; ++w) m = fmaxf(m, s_max[wave >> 1][w]);
+  int sexp = 0;
+  (void)frexpf(m, &sexp);
+
+  DgPassCtx c;
+  c.a = &a;
+  c.s_w = s_w;
+  c.s_dy = s_dy;
+  c.s_exp = s_exp;
+  c.wexp = a.d.packed + (size_t)e * N * ((size_t)K / 2);
+  c.aexp = aexp;
+  c.sexp = sexp;
+  c.tid = tid;
+  c.wave = wave;
+  c.lane = lane;
+  c.i = lane & 31;
+  c.h = lane >> 5;
+  c.N = N;
+  c.K = K;
+  c.bpr = bpr;
+  c.k0 = k0;
+  for (int p0 = r_begin; p0 < r_end; p0 += kDgPassRows) {
+    c.p0 = p0;
+    c.rows = min(kDgPassRows, r_end - p0);
+    int t = 0;
+    if (tid < c.rows) t = a.row_exp[p0 + tid];
+    if (tid < kDgPassRows) s_exp[tid] = t;
+    const bool scaled = __syncthreads_or(t) != 0;
+    switch ((c.rows + 31) / 32) {
+      case 1: dgrad_pass<1, AbsT>(c, scaled); break;
+      case 2: dgrad_pass<2, AbsT>(c, scaled); break;
+      case 3: dgrad_pass<3, AbsT>(c, scaled); break;
+      default: dgrad_pass<4, AbsT>(c, scaled); break;
+    }
+    __syncthreads();  // the next pass reuses the LDS buffers
+  }
+}
+
 // Activation scale exponents, one wavefront per row: per token row of x
 // when `by_token` (fused gather), else per output row r < M with its source
 // (x row r, or its token through the fused gather's slot).  From the
@@ -580,6 +829,23 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
     hipLaunchKernelGGL(tile_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(tile_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad_tile(const DgradArgs& d, const int32_t* row_exp, int rows_min,
+                             hipStream_t stream) {
+  DgradTileKArgs a;
+  a.d = d;
+  a.row_exp = row_exp;
+  a.rows_min = rows_min;
+  a.k_tiles = (d.K + kDgTileK - 1) / kDgTileK;
+  a.n_work = (int)group_slots(d.G, d.M, rows_min) * a.k_tiles;
+  const int grid = ((a.n_work + 7) / 8) * 8;
+  if (grid == 0) return hipSuccess;
+  if (d.abs_bf16)
+    hipLaunchKernelGGL(dgrad_tile_kernel<uint16_t>, dim3(grid), dim3(kDgThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dgrad_tile_kernel<float>, dim3(grid), dim3(kDgThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,11 @@ def library():
                                     vp]
     lib.gnf4_grouped_dgrad_workspace_size.restype = sz
     lib.gnf4_grouped_dgrad_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.gnf4_grouped_dgrad_workspace_size_ex.restype = sz
+    lib.gnf4_grouped_dgrad_workspace_size_ex.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.gnf4_grouped_dgrad_ex.restype = ctypes.c_int
+    lib.gnf4_grouped_dgrad_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
+                                          i32, i32, vp]
     lib.gnf4_grouped_dgrad.restype = ctypes.c_int
     lib.gnf4_grouped_dgrad.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
                                        i32, vp]
@@ -240,9 +245,10 @@ def grouped_gemm_mxfp4(x, packed, scales, group_sizes, group_expert_ids, G=None,
 # ------------------------------------------------------------------ dgrad
 
 def grouped_dgrad(dy, packed, absmax, group_sizes, group_expert_ids, G=None, dx=None,
-                  workspace=None):
+                  workspace=None, path=PATH_AUTO):
     """dx[M, K] (bf16) = per-group dy[rows] @ dequant(W[expert]) -- the
-    activation gradient of grouped_gemm over the same packed stack."""
+    activation gradient of grouped_gemm over the same packed stack.  ``path``:
+    PATH_AUTO, PATH_DECODE (the GEMV kernel) or PATH_TILE (matrix cores)."""
     _need(dy, "dy", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 3)
     _need(absmax, "absmax", absmax.dtype, 3)
@@ -261,13 +267,13 @@ def grouped_dgrad(dy, packed, absmax, group_sizes, group_expert_ids, G=None, dx=
     if dx is None:
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
     _need(dx, "dx", torch.bfloat16, 2)
-    need = library().gnf4_grouped_dgrad_workspace_size(M, N, K, G, E)
+    need = library().gnf4_grouped_dgrad_workspace_size_ex(M, N, K, G, E, path)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().gnf4_grouped_dgrad(
+    _check(library().gnf4_grouped_dgrad_ex(
         _ptr(dy), _ptr(packed), _ptr(absmax), E, N, K, _ptr(group_sizes), _ptr(group_expert_ids),
-        G, M, _ptr(dx), _ptr(workspace), ws_bytes, adt, _stream()), "gnf4_grouped_dgrad")
+        G, M, _ptr(dx), _ptr(workspace), ws_bytes, adt, path, _stream()), "gnf4_grouped_dgrad_ex")
     return dx
 
 

@@ -222,16 +222,28 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
  *   dx                [M, K] bf16 bits out; only rows covered by a valid
  *                     group are written
  *   workspace         device scratch of gnf4_grouped_dgrad_workspace_size()
- *                     bytes for the split-N fp32 partials (16-byte aligned);
- *                     with less, the call runs unsplit (correct, slower)
+ *                     bytes (16-byte aligned): the GEMV path's split-N fp32
+ *                     partials (with less, that path runs unsplit: correct,
+ *                     slower), or the tile path's per-row exponents of dy
+ *                     (4 M bytes rounded up to 256; required)
  *
- * fp32 decode and accumulation, one bf16 rounding; |dx - exact| <= 8e-3
- * |exact| + 1e-3 rms(exact) per element.  Splits are summed in fixed order:
- * deterministic run to run.  Every weight byte is read once per pass of up
- * to 4 rows of dy, so the kernel suits groups of few rows (decode-sized
- * batches); large groups re-read the weights once per 4 rows.
+ * Two kernels meet one contract, |dx - exact| <= 8e-3 |exact| + 1e-3
+ * rms(exact) per element, deterministic run to run:
+ *  - GEMV path: fp32 decode and accumulation, splits of N summed in fixed
+ *    order.  Every weight byte is read once per pass of up to 4 rows of dy,
+ *    so it suits groups of few rows (decode-sized batches).
+ *  - tile path (matrix cores): codes decoded once per 128 rows of a group
+ *    into fp16 scaled by a power of two per 64-column block of K (its largest
+ *    absmax over the N rows), dy rows staged in fp16 with a power of two per
+ *    row, fp16 x fp16 -> fp32 MFMA, the scales applied exactly at the end.
+ *    Needs N % 8 == 0 and a 16-byte aligned dy.  A block whose absmax lies
+ *    2^24 or more below its column block's largest flushes toward zero.
+ * gnf4_grouped_dgrad chooses automatically: the tile path for a batch
+ * averaging at least 32 rows per group (M >= 32 min(G, M)) when dy allows
+ * it, else the GEMV path.
  * Limits: as gnf4_grouped_gemm, plus M * N < 2^31.
- * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_UNSUPPORTED,
+ * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE
+ * (tile path without room for its exponents), GNF4_ERR_UNSUPPORTED,
  * GNF4_ERR_HIP.
  */
 size_t gnf4_grouped_dgrad_workspace_size(int64_t M, int64_t N, int64_t K, int64_t G, int64_t E);
@@ -241,6 +253,21 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
                                const int32_t* group_expert_ids, int64_t G, int64_t M,
                                uint16_t* dx, void* workspace, size_t workspace_bytes,
                                int32_t absmax_dtype, void* stream);
+
+/*
+ * gnf4_grouped_dgrad_ex -- gnf4_grouped_dgrad with the path choice exposed,
+ * for tests and tuning.  `path`: 0 = automatic (as gnf4_grouped_dgrad),
+ * 1 = GEMV path, 2 = tile path (GNF4_ERR_UNSUPPORTED unless N % 8 == 0 and
+ * dy is 16-byte aligned).  The workspace query takes the same `path`.
+ */
+size_t gnf4_grouped_dgrad_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
+                                            int64_t E, int32_t path);
+
+gnf4_status gnf4_grouped_dgrad_ex(const uint16_t* dy, const uint8_t* packed, const void* absmax,
+                                  int64_t E, int64_t N, int64_t K, const int32_t* group_sizes,
+                                  const int32_t* group_expert_ids, int64_t G, int64_t M,
+                                  uint16_t* dx, void* workspace, size_t workspace_bytes,
+                                  int32_t absmax_dtype, int32_t path, void* stream);
 
 /*
  * gnf4_swiglu -- the activation between the two expert projections:

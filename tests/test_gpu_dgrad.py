@@ -1,7 +1,8 @@
 """GPU parity for gnf4_grouped_dgrad (dx = dy . W per group) against the
-fp64 oracle: the workloads' shapes, the grouping boundary cases, the
-unsplit fallback, determinism, and the DSV3 down stack at full size
-(sampled rows).
+fp64 oracle, on the GEMV path and the matrix-core tile path: the workloads'
+shapes, the grouping boundary cases, adversarial absmax, dy rows far outside
+fp16's range, the unsplit fallback, determinism, and the DSV3 down stack at
+full size (sampled rows, automatic path = tile path).
 
 Bar: |dx - o| <= 8e-3 |o| + 1e-3 rms(o) element by element, the forward
 GEMM's bound.
@@ -21,6 +22,13 @@ from test_gpu_full_size import device_stack, host_expert
 
 pytestmark = pytest.mark.gpu
 
+DEC, TILE, AUTO = gnf4.PATH_DECODE, gnf4.PATH_TILE, gnf4.PATH_AUTO
+
+
+def _skip_tile(path, N):
+    if path == TILE and N % 8:
+        pytest.skip("the tile path reads dy in 16-byte chunks (N % 8 == 0)")
+
 
 def _oracle_stack(wl, host, N, K):
     p = np.zeros((wl.E, N, K // 2), np.uint8)
@@ -33,28 +41,35 @@ def _oracle_stack(wl, host, N, K):
 @pytest.mark.parametrize("name,gemm", [("tiny", "w"), ("olmoe", "gate_up"), ("olmoe", "down"),
                                        ("qwen3_t8", "gate_up"), ("gptoss", "gate_up"),
                                        ("gptoss", "down"), ("gptoss_t256", "down")])
-def test_dgrad_workload_shapes(name, gemm):
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_dgrad_workload_shapes(name, gemm, path):
     wl = wls.WORKLOADS[name]
     K, N = wl.gemm(gemm)
+    _skip_tile(path, N)
     logits = wls.router_logits(wl)
     ref = oracle.ref_route_sort(logits, wl.top_k)
     r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
     used = ref["group_expert_ids"][: ref["num_groups"]]
     packed, absmax, host = routed_stack(wl, gemm, used)
     dy = bf16_dev(np.random.default_rng(K + N).standard_normal((wl.M, N)))
-    note(f"dgrad {name}/{gemm} M={wl.M} N={N} K={K}")
-    dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids)
+    note(f"dgrad {name}/{gemm} M={wl.M} N={N} K={K} path={path}")
+    dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids, path=path)
     torch.cuda.synchronize()
     p, a = _oracle_stack(wl, host, N, K)
     o, written = oracle.ref_grouped_dgrad(host_f64(dy), p, a, ref["group_sizes"],
                                           ref["group_expert_ids"])
-    check_gemm(dx, o, written, f"dgrad {name}/{gemm}")
+    check_gemm(dx, o, written, f"dgrad {name}/{gemm} path {path}")
 
 
-def _custom(E, N, K, sizes, ids, M, seed):
+def _custom(E, N, K, sizes, ids, M, seed, w_scale=None, dy_scale=None):
     rng = np.random.default_rng(seed)
     w = wls.bf16_round((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32))
-    dy = wls.bf16_round(rng.standard_normal((M, N)).astype(np.float32))
+    if w_scale is not None:
+        w = wls.bf16_round(w * w_scale)
+    dy = rng.standard_normal((M, N)).astype(np.float32)
+    if dy_scale is not None:
+        dy = dy * dy_scale
+    dy = wls.bf16_round(dy.astype(np.float32))
     packed, absmax = gnf4.pack(bf16_dev(w))
     p, a = oracle.ref_pack(w)
     o, written = oracle.ref_grouped_dgrad(dy, p, a, sizes, ids)
@@ -63,12 +78,12 @@ def _custom(E, N, K, sizes, ids, M, seed):
                 ids=torch.tensor(ids, dtype=torch.int32, device=DEV), M=M, K=K)
 
 
-def _run(c, workspace=None):
+def _run(c, workspace=None, path=AUTO):
     M, K = c["M"], c["K"]
     full = torch.full((M + 2, K), -512.0, dtype=torch.bfloat16, device=DEV)
     dx = full[1:M + 1]
     gnf4.grouped_dgrad(c["dy"], c["packed"], c["absmax"], c["sizes"], c["ids"],
-                       G=c["sizes"].numel(), dx=dx, workspace=workspace)
+                       G=c["sizes"].numel(), dx=dx, workspace=workspace, path=path)
     torch.cuda.synchronize()
     f = full.float().cpu().numpy()
     assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0), "guard rows written"
@@ -77,13 +92,66 @@ def _run(c, workspace=None):
 
 
 @pytest.mark.parametrize("case", sorted(BOUNDARY_CASES))
-def test_dgrad_boundaries(case):
+@pytest.mark.parametrize("path", [AUTO, DEC, TILE])
+def test_dgrad_boundaries(case, path):
     E, N, K, sizes, ids, M = BOUNDARY_CASES[case]
-    note(f"dgrad boundary {case}")
+    _skip_tile(path, N)
+    note(f"dgrad boundary {case} path={path}")
     c = _custom(E, N, K, sizes, ids, M, seed=21)
-    dx = _run(c)
+    dx = _run(c, path=path)
     if c["written"].any():
-        check_gemm(dx, c["o"], c["written"], f"dgrad {case}")
+        check_gemm(dx, c["o"], c["written"], f"dgrad {case} path {path}")
+
+
+def _absmax_scenarios(E, N, K):
+    """Weight magnitudes that stress the tile path's per-column-block scale:
+    blocks alternating 1e-30 / 1e30 along K, one row 1e4 above the others,
+    zero blocks, one large element per block, rows spread over 20 binades."""
+    s = {}
+    a = np.ones((E, N, K), np.float32)
+    for b in range(K // 64):
+        a[:, :, 64 * b:64 * (b + 1)] = 1e-30 if b % 2 else 1e30
+    s["blocks_1e-30_to_1e30"] = a
+    z = np.ones((E, N, K), np.float32)
+    z[:, :, 64:192] = 0.0
+    z[:, 3, :] = 1e4
+    s["zero_blocks_outlier_row"] = z
+    p = np.ones((E, N, K), np.float32)
+    p[:, :, ::64] = 500.0
+    s["one_outlier_per_block"] = p
+    s["rows_over_20_binades"] = np.ones((E, N, K), np.float32) * (
+        2.0 ** -(np.arange(N) % 20)).astype(np.float32)[None, :, None]
+    return s
+
+
+@pytest.mark.parametrize("scenario", sorted(_absmax_scenarios(1, 8, 128)))
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_dgrad_adversarial_absmax(scenario, path):
+    E, N, K, M = 3, 64, 512, 96
+    scale = _absmax_scenarios(E, N, K)[scenario]
+    note(f"dgrad adversarial absmax {scenario} path={path}")
+    c = _custom(E, N, K, [40, 24, 32], [2, 0, 1], M, seed=23, w_scale=scale)
+    dx = _run(c, path=path)
+    check_gemm(dx, c["o"], c["written"], f"dgrad {scenario} path {path}")
+
+
+@pytest.mark.parametrize("scale", [1e-20, 5e4, 1e30])
+def test_dgrad_tile_dy_magnitudes(scale):
+    """dy rows far outside fp16's range mixed with ordinary rows and a zero
+    row; the tile path scales each dy row by its own power of two, so each
+    class meets the bar on its own."""
+    E, N, K, M = 3, 96, 256, 72
+    f = np.ones((M, 1), np.float32)
+    f[::3] = scale
+    f[7] = 0.0
+    c = _custom(E, N, K, [30, 20, 22], [1, 2, 0], M, seed=24, dy_scale=f)
+    note(f"dgrad tile dy magnitude {scale:g}")
+    dx = _run(c, path=TILE)
+    cls = np.zeros(M, bool)
+    cls[::3] = True
+    for what, mask in (("scaled", cls), ("ordinary", ~cls)):
+        check_gemm(dx, c["o"], c["written"] & mask, f"dgrad dy*{scale:g} {what} rows")
+    assert np.all(host_f64(dx)[7] == 0.0)
 
 
 def test_dgrad_unsplit_fallback_and_determinism():
@@ -127,7 +195,8 @@ def test_dgrad_dsv3_down_full_size_sampled_rows():
 
 
 @pytest.mark.parametrize("name,gemm", [("olmoe", "down"), ("gptoss_t256", "down")])
-def test_dgrad_bf16_absmax(name, gemm):
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_dgrad_bf16_absmax(name, gemm, path):
     wl = wls.WORKLOADS[name]
     K, N = wl.gemm(gemm)
     logits = wls.router_logits(wl)
@@ -143,8 +212,8 @@ def test_dgrad_bf16_absmax(name, gemm):
         gnf4.pack(bf16_dev(w), out=(packed[e], absmax[e]))
         p_ref[e], a_ref[e] = oracle.ref_pack(w, absmax_dtype="bf16")
     dy = bf16_dev(np.random.default_rng(9).standard_normal((wl.M, N)))
-    note(f"dgrad bf16 absmax {name}/{gemm}")
-    dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids)
+    note(f"dgrad bf16 absmax {name}/{gemm} path={path}")
+    dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids, path=path)
     torch.cuda.synchronize()
     o, written = oracle.ref_grouped_dgrad(host_f64(dy), p_ref, a_ref, ref["group_sizes"],
                                           ref["group_expert_ids"])
