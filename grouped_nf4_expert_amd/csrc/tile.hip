@@ -506,9 +506,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
 // "grouped-nf4-gemm", "Owns": the grouped packed GEMM and its dgrad).  The
 // contraction runs over N, across the rows of each expert's K-contiguous
 // codes, so the decoded weights are written to LDS transposed, [k][n], and
-// read back as MFMA operands of 8 consecutive n.  A workgroup of 4
-// wavefronts owns (group, 128 columns of K) and walks N in steps of 64; each
-// wavefront owns 32 of the columns for every row of the group (up to 4 row
+// read back as MFMA operands of 8 consecutive n.  A workgroup of 8
+// wavefronts owns (group, 256 columns of K) and walks N in steps of 64; each
+// wavefront owns 32 of the columns for every row of the group (up to 5 row
 // tiles of 32 per pass), so each code is decoded once per pass.
 //  * weights: lane l of wavefront w loads the 16 bytes (32 codes, one
 //    64-code absmax block) at row n0 + l, columns k0 + 32 w, and decodes them
@@ -524,10 +524,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
 // A block whose absmax lies 2^24 or more below its column block's largest
 // flushes toward zero in fp16, the range limit of the forward tile path
 // with the roles of rows and columns exchanged.
-constexpr int kDgThreads = 256;    // 4 wavefronts, 32 output columns each
-constexpr int kDgTileK = 128;      // output columns (of K) per workgroup
+constexpr int kDgThreads = 512;    // 8 wavefronts (two per SIMD), 32 output columns each
+constexpr int kDgTileK = 256;      // output columns (of K) per workgroup
+constexpr int kDgBlocks = kDgTileK / kBlock;  // absmax blocks a tile's columns span
 constexpr int kDgStepN = 64;       // rows of W (contraction) per step
-constexpr int kDgRowTiles = 4;     // 32-row MFMA tiles per pass
+constexpr int kDgRowTiles = 5;     // 32-row MFMA tiles per pass
 constexpr int kDgPassRows = 32 * kDgRowTiles;
 constexpr int kDgLds = kDgStepN + 8;  // fp16 per LDS row: 144 bytes, conflict-free reads
 
@@ -563,9 +564,11 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
   const size_t row_bytes = (size_t)c.K / 2;
   const int kk = c.k0 + 32 * c.wave;  // this wavefront's first code column
   const bool k_ok = kk < c.K;
+  // 16-byte dy chunks per thread: RT * 32 rows x 8 chunks over the threads
+  constexpr int kChunks = (RT * 256 + kDgThreads - 1) / kDgThreads;
   uint4 wr;
   float war;
-  uint4 yr[RT];
+  uint4 yr[kChunks];
   // Loads of step s are issued at the top of step s - 1 and consumed (staged
   // into LDS) at its end, so no loaded register lives across the loop's
   // back edge.
@@ -576,10 +579,10 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
     war = absmax_at(static_cast<const AbsT*>(c.aexp) + (ok ? (size_t)n * c.bpr : 0),
                     ok ? kk / kBlock : 0);
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
+    for (int j = 0; j < kChunks; ++j) {
       const int q = c.tid + kDgThreads * j;
       const int row = q >> 3, nn = step * kDgStepN + 8 * (q & 7);
-      const bool okr = row < c.rows && nn < c.N;
+      const bool okr = q < RT * 256 && row < c.rows && nn < c.N;
       yr[j] = *reinterpret_cast<const uint4*>(d.dy + (okr ? (size_t)(c.p0 + row) * c.N + nn : 0));
     }
   };
@@ -601,8 +604,9 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
+    for (int j = 0; j < kChunks; ++j) {
       const int q = c.tid + kDgThreads * j;
+      if (kChunks * kDgThreads > RT * 256 && q >= RT * 256) break;
       const int row = q >> 3, c8 = q & 7;
       const int nn = step * kDgStepN + 8 * c8;
       const bool okr = row < c.rows && nn < c.N;
@@ -652,11 +656,11 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
 }
 
 template <typename AbsT>
-__global__ __launch_bounds__(kDgThreads, 2) void dgrad_tile_kernel(DgradTileKArgs a) {
+__global__ __launch_bounds__(kDgThreads, 1) void dgrad_tile_kernel(DgradTileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_w[2 * kDgTileK * kDgLds];
   __shared__ __attribute__((aligned(16))) _Float16 s_dy[2 * kDgPassRows * kDgLds];
   __shared__ int s_exp[kDgPassRows];
-  __shared__ float s_max[2][kDgThreads / kWave];
+  __shared__ float s_max[kDgBlocks][kDgThreads / kWave];
 
   // XCD-aware order: consecutive work items land on one XCD.
   const int nb = gridDim.x;
@@ -676,39 +680,38 @@ __global__ __launch_bounds__(kDgThreads, 2) void dgrad_tile_kernel(DgradTileKArg
   const int wave = tid / kWave, lane = tid % kWave;
   const int N = a.d.N, K = a.d.K, bpr = K / kBlock;
   const int k0 = kt * kDgTileK;
-  const int kb0 = k0 / kBlock;  // the tile's two absmax blocks: kb0, kb0 + 1
-  const bool has_b1 = kb0 + 1 < bpr;
+  const int kb0 = k0 / kBlock;  // the tile's absmax blocks: kb0 .. kb0 + 3
   const AbsT* aexp = static_cast<const AbsT*>(a.d.absmax) + (size_t)e * N * bpr;
 
-  // column-block scales: the largest absmax of blocks kb0 and kb0 + 1 over
-  // all N rows (4 independent loads per round per thread)
-  float m0 = 0.0f, m1 = 0.0f;
-  for (int n0 = tid; n0 < N; n0 += 4 * kDgThreads) {
-    float v0[4], v1[4];
+  // column-block scales: the largest absmax of each of the tile's blocks
+  // over all N rows (8 rows per round per thread, all loads issued before
+  // any is used; a row past N re-reads row n0, a block past K block kb0)
+  float mb[kDgBlocks];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+  for (int q = 0; q < kDgBlocks; ++q) mb[q] = 0.0f;
+  for (int n0 = tid; n0 < N; n0 += 8 * kDgThreads) {
+    float v[8][kDgBlocks];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
       const int n = n0 + u * kDgThreads;
       const AbsT* ar = aexp + (size_t)(n < N ? n : n0) * bpr;
-      v0[u] = absmax_at(ar, kb0);
-      v1[u] = absmax_at(ar, has_b1 ? kb0 + 1 : kb0);
+#pragma unroll
+      for (int q = 0; q < kDgBlocks; ++q) v[u][q] = absmax_at(ar, kb0 + q < bpr ? kb0 + q : kb0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      m0 = fmaxf(m0, v0[u]);
-      m1 = fmaxf(m1, v1[u]);
-    }
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int q = 0; q < kDgBlocks; ++q) mb[q] = fmaxf(mb[q], v[u][q]);
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    m0 = fmaxf(m0, __shfl_xor(m0, o, kWave));
-    m1 = fmaxf(m1, __shfl_xor(m1, o, kWave));
-  }
-  if (lane == 0) {
-    s_max[0][wave] = m0;
-    s_max[1][wave] = m1;
-  }
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int q = 0; q < kDgBlocks; ++q) mb[q] = fmaxf(mb[q], __shfl_xor(mb[q], o, kWave));
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < kDgBlocks; ++q) s_max[q][wave] = mb[q];
   __syncthreads();
-  // wavefronts 0, 1 own the columns of block kb0, wavefronts 2, 3 those of kb0 + 1
+  // wavefront w owns columns k0 + 32 w .. + 31, inside block kb0 + w / 2
   float m = 0.0f;
 #pragma unroll
   for (int w = 0; w < kDgThreads / kWave; ++w) m = fmaxf(m, s_max[wave >> 1][w]);
@@ -743,7 +746,8 @@ __global__ __launch_bounds__(kDgThreads, 2) void dgrad_tile_kernel(DgradTileKArg
       case 1: dgrad_pass<1, AbsT>(c, scaled); break;
       case 2: dgrad_pass<2, AbsT>(c, scaled); break;
       case 3: dgrad_pass<3, AbsT>(c, scaled); break;
-      default: dgrad_pass<4, AbsT>(c, scaled); break;
+      case 4: dgrad_pass<4, AbsT>(c, scaled); break;
+      default: dgrad_pass<5, AbsT>(c, scaled); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
