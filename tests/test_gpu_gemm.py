@@ -338,3 +338,32 @@ def test_fused_gather_bad_slots_skip_rows(path):
     assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0)
     assert np.all(f[1:M + 1][~written] == -512.0), "rows with bad slots were written"
     check_gemm(full[1:M + 1], c["y_ref"], written, f"bad slots path {path}")
+
+
+@pytest.mark.parametrize("split_k", [0, 2])
+def test_fused_gather_one_token(split_k):
+    """A single token behind the fused gather (a batch-1 decode step): every
+    valid slot reads token 0, the decode path loads it before the group
+    metadata; rows with invalid slots stay unwritten, groups of one and of
+    several rows (duplicate picks of a caller-built grouping) both work."""
+    E, N, K, T, top_k = 6, 96, 512, 1, 8
+    sizes, ids = [1, 3, 1, 2, 1], [5, 0, 2, 4, 1]
+    M = sum(sizes)
+    slots = np.array([3, 0, 9, 2, 7, -1, 5, 1], dtype=np.int32)   # 9, -1: invalid
+    rng = np.random.default_rng(33)
+    x_tok = wls.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    ok = (slots >= 0) & (slots < T * top_k)
+    x_rows = np.zeros((M, K), np.float32)
+    x_rows[ok] = x_tok[0]
+    c = _custom(E, N, K, sizes, ids, M, seed=34, x=x_rows)
+    written = c["written"] & ok
+    full = torch.full((M + 2, N), -512.0, dtype=torch.bfloat16, device=DEV)
+    note(f"gemm fused gather one token split_k={split_k}")
+    gnf4.grouped_gemm(bf16_dev(x_tok), c["packed"], c["absmax"], c["sizes"], c["ids"],
+                      G=len(sizes), y=full[1:M + 1], path=DEC, split_k=split_k,
+                      sorted_slots=torch.from_numpy(slots).to(DEV), top_k=top_k)
+    torch.cuda.synchronize()
+    f = full.float().cpu().numpy()
+    assert np.all(f[0] == -512.0) and np.all(f[M + 1] == -512.0)
+    assert np.all(f[1:M + 1][~written] == -512.0), "rows with bad slots were written"
+    check_gemm(full[1:M + 1], c["y_ref"], written, f"one token split {split_k}")
