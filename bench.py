@@ -36,6 +36,7 @@ METRIC = "grouped NF4 GEMM effective HBM GB/s (decode) & TFLOP/s (prefill), % ro
 
 
 ABS_BYTES = 4  # bytes per block absmax: 4 (fp32) or 2 (bf16, --absmax-dtype bf16)
+UNFUSED_ROUTE = False  # --unfused-route
 
 
 def gemm_bytes(n_touched, M, N, K):
@@ -78,6 +79,8 @@ def parse():
                     help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
     ap.add_argument("--only", default="",
                     help="comma-separated workload names: restrict --cells / --mxfp4 / --dgrad to them")
+    ap.add_argument("--unfused-route", action="store_true",
+                    help="run the route/sort as its own launch even where it folds into gate_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -144,15 +147,28 @@ def build_layers(wl, L, dev, first_layer=0):
         wsg = gnf4.gemm_workspace_size(wl.M, Ng, Kg, G, wl.E)
         wsd = gnf4.gemm_workspace_size(wl.M, Nd, Kd, G, wl.E)
         ly.wsg = torch.empty(max(wsg, 16), dtype=torch.uint8, device=dev)
+        wsr = gnf4.library().gnf4_route_gemm_one_token_workspace_size(wl.E, wl.top_k, Ng, Kg)
+        ly.wsr = torch.empty(max(wsr, 16), dtype=torch.uint8, device=dev)
         ly.wsd = torch.empty(max(wsd, 16), dtype=torch.uint8, device=dev)
         layers.append(ly)
     torch.cuda.synchronize()
     return layers
 
 
+def fused_route(wl):
+    """A single token with at most 64 experts: the route/sort is folded into
+    the gate_up launch (gnf4_route_gemm_one_token), unless --unfused-route."""
+    return wl.T == 1 and wl.E <= 64 and not UNFUSED_ROUTE
+
+
 def gate_up(wl, ly):
-    """gate_up GEMM reading the token rows through the sort (fused gather)."""
+    """gate_up GEMM reading the token rows through the sort (fused gather);
+    with the route folded in, the same launch also routes the token."""
     from grouped_nf4_expert_amd import gnf4
+    if fused_route(wl):
+        gnf4.route_gemm_one_token(ly.logits, ly.x, ly.pg, ly.ag, wl.top_k, buffers=ly.route,
+                                  y=ly.yg, workspace=ly.wsr)
+        return
     r = ly.route.result
     gnf4.grouped_gemm(ly.x, ly.pg, ly.ag, r.group_sizes, r.group_expert_ids, G=ly.G, y=ly.yg,
                       workspace=ly.wsg, sorted_slots=r.sorted_slots, top_k=wl.top_k)
@@ -160,8 +176,10 @@ def gate_up(wl, ly):
 
 def run_layer(wl, ly):
     from grouped_nf4_expert_amd import gnf4
-    r = gnf4.route_sort(ly.logits, wl.top_k, ly.route)
+    if not fused_route(wl):
+        gnf4.route_sort(ly.logits, wl.top_k, ly.route)
     gate_up(wl, ly)
+    r = ly.route.result
     gnf4.grouped_gemm(ly.xd, ly.pd, ly.ad, r.group_sizes, r.group_expert_ids, G=ly.G, y=ly.yd,
                       workspace=ly.wsd)
 
@@ -481,7 +499,8 @@ def time_glue(path, dev, reps=10):
 
 
 KERNEL_SOURCES = ("grouped_nf4_expert_amd/csrc/decode.hip",
-                  "grouped_nf4_expert_amd/csrc/gnf4_internal.h")
+                  "grouped_nf4_expert_amd/csrc/gnf4_internal.h",
+                  "grouped_nf4_expert_amd/csrc/route_core.h")
 
 
 def kernel_digest():
@@ -547,9 +566,10 @@ def summarize(d):
 
 
 def main():
-    global ABS_BYTES
+    global ABS_BYTES, UNFUSED_ROUTE
     args = parse()
     ABS_BYTES = 2 if args.absmax_dtype == "bf16" else 4
+    UNFUSED_ROUTE = args.unfused_route
     if args.summarize:
         summarize(args.summarize)
         return
@@ -611,7 +631,9 @@ def main():
     touched = [[int(ly.route.result.num_groups.cpu()[0]) for ly in layers] for layers in sets]
     set_bytes = [sum(route_bytes(wl.T, wl.E, wl.top_k) + gemm_bytes(n, wl.M, Ng, Kg) +
                      gemm_bytes(n, wl.M, Nd, Kd) for n in t) for t in touched]
-    dom_bytes = [gemm_bytes(n, wl.M, Ng, Kg) for t in touched for n in t]
+    # the dominant launch: gate_up, plus the route/sort's bytes when it is folded in
+    dom_route = route_bytes(wl.T, wl.E, wl.top_k) if fused_route(wl) else 0
+    dom_bytes = [gemm_bytes(n, wl.M, Ng, Kg) + dom_route for t in touched for n in t]
 
     flat = [ly for layers in sets for ly in layers]
 
@@ -697,7 +719,9 @@ def main():
         "config": {
             "workload": f"{wl.name}: E={wl.E} top_k={wl.top_k} T={wl.T} M={wl.M}, gate_up "
                         f"K={Kg} N={Ng} + down K={Kd} N={Nd}, {L} layers of distinct weights "
-                        f"per step (route/sort + gate_up with fused gather + down)",
+                        + ("per step (route/sort folded into gate_up with fused gather + down)"
+                           if fused_route(wl) else
+                           "per step (route/sort + gate_up with fused gather + down)"),
             "weights": f"NF4 (block 64, {'bf16' if ABS_BYTES == 2 else 'fp32'} absmax)",
             "activations": "bf16",
             "global_batch": wl.T, "layers": L, "parallelism": "none (1 GPU)",
@@ -707,7 +731,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode-path grouped GEMM (gate_up, fused row gather), "
+            "kernel": "decode-path grouped GEMM (gate_up, fused row gather"
+                      + (", route/sort folded in" if fused_route(wl) else "") + "), "
                       f"{2 * len(flat)} launches back to back per HIP graph replay",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -6,6 +6,7 @@
 
 #include "dgrad_tile.h"
 #include "gnf4_internal.h"
+#include "route_core.h"
 
 namespace gnf4 {
 
@@ -403,6 +404,95 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
   }
   return gemm_common(x, packed, scales, kScaleE8M0, E, N, K, group_sizes, group_expert_ids, G, M,
                      y, workspace, workspace_bytes, path, split_k, stream);
+}
+
+// The routed one-token GEMM's decode plan: top_k rows, one per pick.
+static DecodePlan route_gemm_plan(int32_t top_k, int64_t N, int64_t K) {
+  return plan_decode(top_k, N, K, top_k, 0, device_cu_count());
+}
+
+size_t gnf4_route_gemm_one_token_workspace_size(int64_t E, int32_t top_k, int64_t N, int64_t K) {
+  (void)E;
+  if (top_k < 1 || N <= 0 || K < kBlock) return 0;
+  return decode_workspace_bytes(route_gemm_plan(top_k, N, K), top_k, N);
+}
+
+gnf4_status gnf4_route_gemm_one_token(const float* logits, int64_t E, int32_t top_k,
+                                      const uint16_t* x, const uint8_t* packed,
+                                      const void* absmax, int32_t absmax_dtype, int64_t N,
+                                      int64_t K, uint16_t* y, int32_t* topk_ids, float* topk_w,
+                                      int32_t* expert_offsets, int32_t* sorted_slots,
+                                      int32_t* slot_rows, int32_t* group_sizes,
+                                      int32_t* group_expert_ids, int32_t* num_groups,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (E < 1 || top_k < 1 || top_k > E || N <= 0 || K < kBlock || K % kBlock != 0)
+    return GNF4_ERR_INVALID_ARG;
+  // one expert per lane of the ranking wavefront; top_k as gnf4_route_sort
+  if (E > 64 || top_k > 32) return GNF4_ERR_UNSUPPORTED;
+  if (N * (K / 2) >= ((int64_t)1 << 31) || E * N >= ((int64_t)1 << 31)) return GNF4_ERR_UNSUPPORTED;
+  if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  const void* out4[] = {topk_ids, topk_w, expert_offsets, sorted_slots, group_sizes,
+                        group_expert_ids, num_groups, logits};
+  for (const void* p : out4)
+    if (!p || !aligned(p, 4)) return GNF4_ERR_INVALID_ARG;
+  if (!x || !packed || !absmax || !y) return GNF4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, dtype_bytes(absmax_dtype)) ||
+      !aligned(y, 2) || (slot_rows && !aligned(slot_rows, 4)))
+    return GNF4_ERR_INVALID_ARG;
+  for (const void* p : out4)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  const void* more[] = {x, packed, absmax, y};
+  for (const void* p : more)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  if (slot_rows && !is_device_ptr(slot_rows)) return GNF4_ERR_NOT_DEVICE_PTR;
+
+  GemmArgs a{};
+  a.x = x;
+  a.packed = packed;
+  a.absmax = absmax;
+  a.abs_bf16 = absmax_dtype == GNF4_DTYPE_BF16;
+  a.mxfp4 = false;
+  a.sizes = group_sizes;       // written by the launch; read by a split-K reduce
+  a.ids = group_expert_ids;
+  a.slots = sorted_slots;
+  a.slot_div = top_k;
+  a.T = 1;
+  a.y = y;
+  a.partial = nullptr;
+  a.row_exp = nullptr;
+  a.E = (int)E;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)E;
+  a.M = top_k;
+  a.rows_max_decode = INT_MAX;
+  a.rows_min_tile = INT_MAX;
+  DecodePlan p = route_gemm_plan(top_k, N, K);
+  if (p.L == 0) return GNF4_ERR_UNSUPPORTED;
+  const size_t need = decode_workspace_bytes(p, top_k, N);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) {
+      p = plan_decode(top_k, N, K, top_k, 1, device_cu_count());  // no room to split: one pass
+      if (p.L == 0) return GNF4_ERR_WORKSPACE;
+    } else {
+      if (!aligned(workspace, 16)) return GNF4_ERR_INVALID_ARG;
+      if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
+      a.partial = static_cast<float*>(workspace);
+    }
+  }
+  RouteOneOut ro;
+  ro.E = (int)E;
+  ro.K = top_k;
+  ro.topk_ids = topk_ids;
+  ro.topk_w = topk_w;
+  ro.offsets = expert_offsets;
+  ro.sorted = sorted_slots;
+  ro.rows = slot_rows;
+  ro.gsizes = group_sizes;
+  ro.gids = group_expert_ids;
+  ro.ngroups = num_groups;
+  const hipError_t e = launch_decode_routed(a, p, logits, ro, (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
 gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,

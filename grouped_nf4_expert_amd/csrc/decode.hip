@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "gnf4_internal.h"
+#include "route_core.h"
 
 namespace gnf4 {
 namespace {
@@ -58,6 +59,10 @@ struct DecodeKArgs {
   GemmArgs g;
   int S, cps, cpr, rows_per_block;
   double inv_slot_div;  // 1 / slot_div, for the fused gather's row index
+  // Routing folded into the launch (one token, E <= 64): the router logits
+  // [E] and the route/sort outputs that workgroup (0, 0, 0) writes.
+  const float* route_logits;
+  RouteOneOut ro;
 };
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* out) {
@@ -230,7 +235,7 @@ __device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
 // table when the gather is fused), (2) the first row chunk's activations,
 // (3) every weight chunk of the lane, step by step; the decode then consumes
 // the weights in the same order.
-template <int L, int NU, int R, int STEPS, typename AbsT>
+template <int L, int NU, int R, int STEPS, typename AbsT, bool ROUTED = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
@@ -243,10 +248,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // (1) metadata: the slot table (issued first, independent of the group)
   // and the group this workgroup serves
   int my_slot = 0;
-  if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
   GroupRef gr;
-  if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y, gr))
-    return;
+  if constexpr (ROUTED) {
+    // One token routed in the launch.  Lane e holds expert e's key, as the
+    // route/sort kernels build it (rank_token); its rank, the number of
+    // larger keys, is counted by the wavefronts together, each against
+    // 64 / kWaves of the keys, and summed through LDS: the same integers
+    // rank_token gives.  Group j is the j-th pick in expert order, one row
+    // (row j, token 0).
+    constexpr int kKeys = kWave / kWaves;
+    static_assert(kKeys * kWaves == kWave, "the keys split evenly over the wavefronts");
+    __shared__ int s_part[kWaves][kWave];
+    const int E = a.ro.E;
+    float val[1];
+    int rank[1];
+    val[0] = lane < E ? a.route_logits[lane] : 0.0f;
+    const uint64_t key = lane < E ? (((uint64_t)float_key(val[0]) << 32) |
+                                     (uint32_t)(0xffffffffu - (uint32_t)lane))
+                                  : 0ull;
+    int part = 0;
+#pragma unroll
+    for (int q = 0; q < kKeys; ++q) part += readlane64(key, kKeys * wave + q) > key ? 1 : 0;
+    s_part[wave][lane] = part;
+    __syncthreads();
+    rank[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) rank[0] += s_part[w][lane];
+    const int j = blockIdx.y;
+    uint64_t m = __ballot(rank[0] < a.ro.K);
+    for (int q = 0; q < j; ++q) m &= m - 1;  // uniform: j < K picks
+    gr.g = j;
+    gr.size = 1;
+    gr.expert = __ffsll((unsigned long long)m) - 1;
+    gr.row = j;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0)
+      route_one_token_write<1>(a.ro, lane, val, rank);
+  } else {
+    if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
+    if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y,
+                    gr))
+      return;
+  }
   const int s = blockIdx.z;
   const int team = lane / L, tl = lane % L;
   const int N = a.g.N, K = a.g.K;
@@ -275,6 +317,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     for (int r = 0; r < R; ++r) {
       const int row = r0 + r;
       xrow[r] = row < r_end ? row : -1;
+      if constexpr (ROUTED) {
+        xrow[r] = row < r_end ? 0 : -1;  // every pick reads the one token
+        continue;
+      }
       if (gather && row < r_end) {
         const int slot = slots_in_lanes ? __builtin_amdgcn_readlane(my_slot, row) : a.g.slots[row];
         xrow[r] = (slot >= 0 && slot < slot_lim) ? div_slot(slot, a.g.slot_div, a.inv_slot_div) : -1;
@@ -428,12 +474,29 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
   }
 }
 
-template <int L, int NU, int R, int STEPS, typename AbsT>
+template <int L, int NU, int R, int STEPS, typename AbsT, bool ROUTED = false>
 hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.n_tiles, (unsigned)group_slots(a.g.G, a.g.M, 1), (unsigned)p.S);
   const size_t lds = (size_t)R * (size_t)(p.cps + 1) * 128;
-  hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS, AbsT>), grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS, AbsT, ROUTED>), grid, dim3(kThreads), lds,
+                     stream, a);
   return hipGetLastError();
+}
+
+// The routed launch: one activation row per group (R = 1).
+template <int L, typename AbsT>
+hipError_t launch_L_routed(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (p.R != 1) return hipErrorInvalidValue;
+  switch (p.steps * 16 + p.NU) {
+    case 16 + 4: return launch_one<L, 4, 1, 1, AbsT, true>(a, p, stream);
+    case 16 + 2: return launch_one<L, 2, 1, 1, AbsT, true>(a, p, stream);
+    case 16 + 1: return launch_one<L, 1, 1, 1, AbsT, true>(a, p, stream);
+    case 32 + 2: return launch_one<L, 2, 1, 2, AbsT, true>(a, p, stream);
+    case 32 + 1: return launch_one<L, 1, 1, 2, AbsT, true>(a, p, stream);
+    case 48 + 1: return launch_one<L, 1, 1, 3, AbsT, true>(a, p, stream);
+    case 64 + 1: return launch_one<L, 1, 1, 4, AbsT, true>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // rows per lane times activation rows at most kMaxLoads (accumulators)
@@ -554,7 +617,7 @@ size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N) {
   return p.S > 1 ? (size_t)p.S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t stream) {
+static DecodeKArgs decode_args(const GemmArgs& g, const DecodePlan& p) {
   DecodeKArgs a;
   a.g = g;
   a.S = p.S;
@@ -562,6 +625,49 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
   a.cpr = g.K / 32;
   a.rows_per_block = p.rows_per_block;
   a.inv_slot_div = 1.0 / (double)(g.slot_div > 0 ? g.slot_div : 1);
+  a.route_logits = nullptr;
+  a.ro = RouteOneOut{};
+  return a;
+}
+
+static hipError_t launch_reduce(const DecodeKArgs& a, hipStream_t stream) {
+  const GemmArgs& g = a.g;
+  const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)group_slots(g.G, g.M, 1));
+  hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_routed(const GemmArgs& g, const DecodePlan& p, const float* logits,
+                                const RouteOneOut& ro, hipStream_t stream) {
+  DecodeKArgs a = decode_args(g, p);
+  a.route_logits = logits;
+  a.ro = ro;
+  hipError_t err;
+  if (g.abs_bf16) {
+    switch (p.L) {
+      case 64: err = launch_L_routed<64, uint16_t>(a, p, stream); break;
+      case 32: err = launch_L_routed<32, uint16_t>(a, p, stream); break;
+      case 16: err = launch_L_routed<16, uint16_t>(a, p, stream); break;
+      case 8: err = launch_L_routed<8, uint16_t>(a, p, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (p.L) {
+      case 64: err = launch_L_routed<64, float>(a, p, stream); break;
+      case 32: err = launch_L_routed<32, float>(a, p, stream); break;
+      case 16: err = launch_L_routed<16, float>(a, p, stream); break;
+      case 8: err = launch_L_routed<8, float>(a, p, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // the split-K reduce runs after the launch: the groups and slots it reads
+  // are the route/sort outputs the launch wrote
+  if (err != hipSuccess || p.S == 1) return err;
+  return launch_reduce(a, stream);
+}
+
+hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t stream) {
+  DecodeKArgs a = decode_args(g, p);
   hipError_t err;
   if (g.mxfp4) {
     switch (p.L) {
@@ -589,9 +695,7 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
     }
   }
   if (err != hipSuccess || p.S == 1) return err;
-  const dim3 grid((unsigned)((g.N + kThreads - 1) / kThreads), (unsigned)group_slots(g.G, g.M, 1));
-  hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_reduce(a, stream);
 }
 
 }  // namespace gnf4

@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include "gnf4_internal.h"
+#include "route_core.h"
 
 namespace gnf4 {
 namespace {
@@ -53,54 +54,6 @@ struct RouteArgs {
   int32_t* ws;       // [n_chunks, E] per-chunk counts, then per-chunk bases
   int n_chunks;
 };
-
-// Order-preserving unsigned key of a float; -0.0 is folded onto +0.0 so the
-// two compare equal (and the lower id wins), as float comparison does.
-__device__ __forceinline__ uint32_t float_key(float v) {
-  const uint32_t u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v += __int_as_float((int)dpp_u32<0xB1, 0xF>(0u, __float_as_uint(v)));
-  v += __int_as_float((int)dpp_u32<0x4E, 0xF>(0u, __float_as_uint(v)));
-  v += __int_as_float((int)dpp_u32<0x141, 0xF>(0u, __float_as_uint(v)));
-  v += __int_as_float((int)dpp_u32<0x140, 0xF>(0u, __float_as_uint(v)));
-  v += __int_as_float((int)dpp_u32<0x142, 0xA>(0u, __float_as_uint(v)));
-  v += __int_as_float((int)dpp_u32<0x143, 0xC>(0u, __float_as_uint(v)));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// Ranks of one token's E logits.  Entry s of a lane is expert lane + 64 s;
-// rank = number of better entries.  Returns the logits in `val`.
-template <int EPL>
-__device__ __forceinline__ void rank_token(const float* __restrict__ row, int E, int lane,
-                                           float (&val)[EPL], int (&rank)[EPL]) {
-  uint64_t key[EPL];
-#pragma unroll
-  for (int s = 0; s < EPL; ++s) {
-    const int e = lane + kWave * s;
-    val[s] = (e < E) ? row[e] : 0.0f;
-    key[s] = (e < E) ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
-                     : 0ull;
-    rank[s] = 0;
-  }
-#pragma unroll
-  for (int s2 = 0; s2 < EPL; ++s2) {
-    if (kWave * s2 >= E) break;
-    for (int j = 0; j < kWave; ++j) {
-      const uint64_t kj = readlane64(key[s2], j);
-#pragma unroll
-      for (int s = 0; s < EPL; ++s) rank[s] += (kj > key[s]) ? 1 : 0;
-    }
-  }
-}
 
 // Top-k of one token: ids/weights to global memory (and ids to LDS).
 template <int EPL>
@@ -147,48 +100,18 @@ __global__ __launch_bounds__(kWave) void route_one_token_kernel(RouteArgs a) {
   float val[EPL];
   int rank[EPL];
   rank_token<EPL>(a.logits, a.E, lane, val, rank);
-  float vbest = 0.0f;
-  uint64_t sel[EPL];
-#pragma unroll
-  for (int s = 0; s < EPL; ++s) {
-    const uint64_t has = __ballot(rank[s] == 0);
-    if (has) vbest = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[s]),
-                                                              __ffsll((unsigned long long)has) - 1));
-    sel[s] = __ballot(rank[s] < a.K);
-  }
-  float ex[EPL];
-  float part = 0.0f;
-#pragma unroll
-  for (int s = 0; s < EPL; ++s) {
-    ex[s] = (rank[s] < a.K) ? expf(val[s] - vbest) : 0.0f;
-    part += ex[s];
-  }
-  const float sum = wave_sum_f32(part);
-  const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  int before = 0;  // picks with a lower expert id than entry (s, lane)
-#pragma unroll
-  for (int s = 0; s < EPL; ++s) {
-    const int e = lane + kWave * s;
-    const int pos = before + __popcll(sel[s] & lt);
-    if (e < a.E) a.offsets[e] = pos;
-    if (rank[s] < a.K) {
-      a.topk_ids[rank[s]] = e;
-      a.topk_w[rank[s]] = ex[s] / sum;
-      a.sorted[pos] = rank[s];  // slot t * k + j with t = 0
-      if (a.rows) a.rows[rank[s]] = pos;
-      a.gsizes[pos] = 1;
-      a.gids[pos] = e;
-    }
-    before += __popcll(sel[s]);
-  }
-  if (lane == 0) {
-    a.offsets[a.E] = a.K;
-    a.ngroups[0] = a.K;
-  }
-  for (int i = a.K + lane; i < a.E; i += kWave) {
-    a.gsizes[i] = 0;
-    a.gids[i] = 0;
-  }
+  RouteOneOut o;
+  o.E = a.E;
+  o.K = a.K;
+  o.topk_ids = a.topk_ids;
+  o.topk_w = a.topk_w;
+  o.offsets = a.offsets;
+  o.sorted = a.sorted;
+  o.rows = a.rows;
+  o.gsizes = a.gsizes;
+  o.gids = a.gids;
+  o.ngroups = a.ngroups;
+  route_one_token_write<EPL>(o, lane, val, rank);
 }
 
 // Wave 0: exclusive scan of cnt[0..E) into base[] (LDS) and offsets[] (global),

@@ -69,6 +69,11 @@ def library():
     lib.gnf4_grouped_dgrad_ex.restype = ctypes.c_int
     lib.gnf4_grouped_dgrad_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
                                           i32, i32, vp]
+    lib.gnf4_route_gemm_one_token_workspace_size.restype = sz
+    lib.gnf4_route_gemm_one_token_workspace_size.argtypes = [i64, i32, i64, i64]
+    lib.gnf4_route_gemm_one_token.restype = ctypes.c_int
+    lib.gnf4_route_gemm_one_token.argtypes = [vp, i64, i32, vp, vp, vp, i32, i64, i64, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gnf4_grouped_dgrad.restype = ctypes.c_int
     lib.gnf4_grouped_dgrad.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, sz,
                                        i32, vp]
@@ -205,6 +210,41 @@ def route_sort(logits, top_k, buffers=None):
         _ptr(r.num_groups), _ptr(buffers.workspace), buffers.ws_bytes, _stream()),
         "gnf4_route_sort")
     return r
+
+
+def route_gemm_one_token(logits, x, packed, absmax, top_k, buffers=None, y=None,
+                         workspace=None):
+    """A batch-1 decode step's route/sort and grouped GEMM in one launch:
+    ``logits`` [1, E] fp32 (E <= 64), ``x`` [1, K] bf16, the packed stack as
+    grouped_gemm takes it.  Returns (y [top_k, N] in grouped order, the
+    RouteResult written into ``buffers``, as route_sort gives for T = 1)."""
+    _need(logits, "logits", torch.float32, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(absmax, "absmax", absmax.dtype, 3)
+    adt = _absmax_dtype(absmax)
+    T, E = logits.shape
+    if T != 1 or x.shape[0] != 1:
+        raise ValueError("route_gemm_one_token routes exactly one token")
+    E_w, N, half_k = packed.shape
+    K = 2 * half_k
+    if E_w != E or x.shape[1] != K or absmax.shape != (E, N, K // 64):
+        raise ValueError("logits/x/packed/absmax shapes do not agree")
+    if buffers is None:
+        buffers = RouteBuffers(1, E, top_k, logits.device)
+    r = buffers.result
+    if y is None:
+        y = torch.empty((top_k, N), dtype=torch.bfloat16, device=x.device)
+    need = library().gnf4_route_gemm_one_token_workspace_size(E, top_k, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().gnf4_route_gemm_one_token(
+        _ptr(logits), E, top_k, _ptr(x), _ptr(packed), _ptr(absmax), adt, N, K, _ptr(y),
+        _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.expert_offsets), _ptr(r.sorted_slots),
+        _ptr(r.slot_rows), _ptr(r.group_sizes), _ptr(r.group_expert_ids), _ptr(r.num_groups),
+        _ptr(workspace), ws_bytes, _stream()), "gnf4_route_gemm_one_token")
+    return y, r
 
 
 # ------------------------------------------------------------------ MXFP4

@@ -152,6 +152,48 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gnf4_route_gemm_one_token -- a batch-1 decode step's routing folded into
+ * the grouped GEMM's launch: the route/sort of one token (every output as
+ * gnf4_route_sort writes them for T = 1, bit for bit) and
+ * y[j, :] = x[0, :] . dequant(W[e_j])^T for its picks e_j in ascending
+ * expert id, in one launch.
+ *
+ * Landing page "grouped-nf4-gemm", "Use this when" (router softmax and top-k
+ * folded into one decode-step launch); the GEMM as gnf4_grouped_gemm_gather
+ * with T = 1.  Every workgroup ranks the logits itself (the same code as
+ * gnf4_route_sort) and takes its expert from the picks; one writes the
+ * route/sort outputs, which the down projection and gnf4_combine then read.
+ *
+ *   logits            [E] fp32 router logits of the token (finite)
+ *   x                 [1, K] bf16 bits: the token's activations (16-byte aligned)
+ *   packed, absmax    [E, N, K/2] uint8 and [E, N, K/64] fp32 or bf16 bits
+ *                     (`absmax_dtype`)
+ *   y                 [top_k, N] bf16 bits out: row j for the j-th pick in
+ *                     ascending expert id (the grouped order)
+ *   topk_ids ... num_groups: as gnf4_route_sort for T = 1 (slot_rows optional)
+ *   workspace         device scratch of gnf4_route_gemm_one_token_workspace_size()
+ *                     bytes for split-K partials (16-byte aligned); with
+ *                     less the call runs unsplit
+ *
+ * Limits: 1 <= E <= 64 (GNF4_ERR_UNSUPPORTED above: one expert per lane of
+ * the ranking wavefront), 1 <= top_k <= min(E, 32) as gnf4_route_sort,
+ * K % 64 == 0, N * K/2 < 2^31.
+ * Tolerance and determinism as gnf4_grouped_gemm.  Errors:
+ * GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_UNSUPPORTED,
+ * GNF4_ERR_WORKSPACE, GNF4_ERR_HIP.
+ */
+size_t gnf4_route_gemm_one_token_workspace_size(int64_t E, int32_t top_k, int64_t N, int64_t K);
+
+gnf4_status gnf4_route_gemm_one_token(const float* logits, int64_t E, int32_t top_k,
+                                      const uint16_t* x, const uint8_t* packed,
+                                      const void* absmax, int32_t absmax_dtype, int64_t N,
+                                      int64_t K, uint16_t* y, int32_t* topk_ids, float* topk_w,
+                                      int32_t* expert_offsets, int32_t* sorted_slots,
+                                      int32_t* slot_rows, int32_t* group_sizes,
+                                      int32_t* group_expert_ids, int32_t* num_groups,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gnf4_gather_rows -- build the grouped activations from token rows:
  * x_sorted[r, :] = x[sorted_slots[r] / top_k, :] for r < M.
  *

@@ -85,6 +85,25 @@ def test_route_rejects_bad_arguments(lib):
     assert lib.gnf4_route_sort(NULL, 4, 8, 2, *args) == 1        # null logits
 
 
+def test_route_gemm_one_token_rejects_bad_arguments(lib):
+    f = lib.gnf4_route_gemm_one_token
+    args = [None, 64, 8, None, None, None, 0, 256, 512, None, None, None, None, None, None, None,
+            None, None, None, 0, None]
+    bad_e = list(args)
+    bad_e[1] = 65                       # more experts than lanes of the ranking wavefront
+    assert f(*bad_e) == 3               # GNF4_ERR_UNSUPPORTED
+    bad_k = list(args)
+    bad_k[2] = 65                       # top_k above E
+    assert f(*bad_k) == 1               # GNF4_ERR_INVALID_ARG
+    big_k = list(args)
+    big_k[2] = 33                       # top_k above gnf4_route_sort's 32
+    assert f(*big_k) == 3
+    bad_kdim = list(args)
+    bad_kdim[8] = 100                   # K not a multiple of 64
+    assert f(*bad_kdim) == 1
+    assert f(*args) == 1                # null pointers
+
+
 def test_gemm_rejects_bad_arguments(lib):
     def call(**kw):
         a = dict(x=FAKE, p=FAKE, a=FAKE, E=4, N=64, K=128, s=FAKE, i=FAKE, G=2, M=8, y=FAKE,
