@@ -574,7 +574,7 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "bench.py measures one GPU; it has no multi-GPU path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
