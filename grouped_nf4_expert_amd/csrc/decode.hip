@@ -51,7 +51,14 @@ constexpr int kWaves = kThreads / kWave;
 // Staged activations per workgroup: R rows x (chunks + 1) slots of 128 bytes
 // (32 fp32) at most, i.e. 40 KB.
 constexpr int kXSlots = 320;
-constexpr int kXBatch = 2;      // 16-byte bf16 pieces per thread per staging round
+// 16-byte bf16 pieces per thread per staging round for a kernel whose lanes
+// cover at most L * steps chunks of R rows (4 pieces per chunk and row, and
+// R * (chunks + 1) <= kXSlots): one round stages them all, so no load loop
+// sits between the weight loads and the decode.
+constexpr int x_batch(int R, int L, int steps) {
+  const int pieces = 4 * R * L * steps < 4 * kXSlots ? 4 * R * L * steps : 4 * kXSlots;
+  return (pieces + kThreads - 1) / kThreads;
+}
 constexpr int kMaxLoads = 4;    // weight chunks in flight per lane (NU * steps)
 constexpr int kMaxSteps = 4;
 
@@ -127,6 +134,13 @@ __device__ __forceinline__ void e2m1_pair(uint32_t d, float& first, float& secon
   second = v.y;
 }
 
+// Every lane issues every load, from row 0 / chunk 0 of the expert where its
+// own row or chunk does not exist; what it loads there is never used (a lane
+// past the K range skips the decode, and rows past N are never stored).
+// Loads in branches, or a zeroing of their registers, would make the
+// compiler wait for all of them (it cannot count loads that may not have
+// been issued) before the activations staged ahead of them and before the
+// first row's decode.
 template <int NU, typename AbsT>
 __device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* aexp,
                                              size_t row_bytes, int bpr, int N, int n_base, int c,
@@ -134,16 +148,17 @@ __device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* ae
 #pragma unroll
   for (int j = 0; j < NU; ++j) {
     const int n = n_base + j;
-    if (valid && n < N) {
-      wq[j] = *reinterpret_cast<const uint4*>(wexp + (size_t)n * row_bytes + 16 * (size_t)c);
-      if constexpr (kMxfp4<AbsT>)
-        av[j] = e8m0_to_f32(aexp[(size_t)n * (2 * bpr) + c]);  // one scale per chunk
-      else
-        av[j] = absmax_at(aexp, (size_t)n * bpr + (c >> 1));
-    } else {
-      wq[j] = make_uint4(0, 0, 0, 0);
-      av[j] = 0.0f;
-    }
+    const bool ok = valid && n < N;
+    const size_t nn = ok ? (size_t)n : 0;
+    const size_t cc = ok ? (size_t)c : 0;
+    const uint4 q = *reinterpret_cast<const uint4*>(wexp + nn * row_bytes + 16 * cc);
+    float v;
+    if constexpr (kMxfp4<AbsT>)
+      v = e8m0_to_f32(aexp[nn * (2 * bpr) + cc]);  // one scale per chunk
+    else
+      v = absmax_at(aexp, nn * bpr + (cc >> 1));
+    wq[j] = q;
+    av[j] = v;
   }
 }
 
@@ -152,12 +167,12 @@ __device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* ae
 // pieces; piece p sits at 16-byte slot (r * 8 + p) * P + c with P = ncs + 1
 // (one pad slot per plane).  The lanes of a team read piece p of
 // consecutive chunks, i.e. consecutive slots: conflict-free.  A thread moves
-// up to kXBatch 16-byte bf16 pieces (= 2 fp32 pieces each) per round; the
-// first round's loads are issued before the weight loads and stored after.
-template <int R>
+// up to XB 16-byte bf16 pieces (= 2 fp32 pieces each) per round; the first
+// round's loads are issued before the weight loads and stored after.
+template <int R, int XB>
 struct XStage {
   int ncs, plane, c_begin, per_row;
-  uint4 v[kXBatch];
+  uint4 v[XB];
 
   __device__ __forceinline__ void init(int c_begin_, int ncs_) {
     c_begin = c_begin_;
@@ -173,7 +188,7 @@ struct XStage {
   }
   __device__ __forceinline__ void load(const uint16_t* x, int K, const int (&xrow)[R], int base) {
 #pragma unroll
-    for (int u = 0; u < kXBatch; ++u) {
+    for (int u = 0; u < XB; ++u) {
       const int idx = base + (int)threadIdx.x + u * kThreads;
       v[u] = make_uint4(0, 0, 0, 0);
       if (idx < R * per_row) {
@@ -191,7 +206,7 @@ struct XStage {
   }
   __device__ __forceinline__ void store(float4* s_x, int base) const {
 #pragma unroll
-    for (int u = 0; u < kXBatch; ++u) {
+    for (int u = 0; u < XB; ++u) {
       const int idx = base + (int)threadIdx.x + u * kThreads;
       if (idx < R * per_row) {
         const int r = row_of(idx);
@@ -206,7 +221,7 @@ struct XStage {
     }
   }
   __device__ __forceinline__ void all(const uint16_t* x, int K, const int (&xrow)[R], float4* s_x) {
-    for (int base = 0; base < R * per_row; base += kXBatch * kThreads) {
+    for (int base = 0; base < R * per_row; base += XB * kThreads) {
       load(x, K, xrow, base);
       store(s_x, base);
     }
@@ -225,6 +240,49 @@ __device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
   if ((long long)(q + 1) * d <= n) ++q;
   if ((long long)q * d > n) --q;
   return q;
+}
+
+// The terms of one weight dword (8 codes, 4 bytes; a byte's high nibble is
+// its first element) against its 8 activations of R rows, added to pr.
+template <int R, typename AbsT>
+__device__ __forceinline__ void dword_terms(uint32_t d, const float (&xw)[R][8], const float* lut,
+                                            float (&pr)[R]) {
+  float vh[4], vl[4];  // the two elements of each byte: vh the first, vl the second
+  if constexpr (kMxfp4<AbsT>) {
+    // E2M1 through the hardware convert (first element = low nibble)
+    e2m1_pair<0>(d, vh[0], vl[0]);
+    e2m1_pair<1>(d, vh[1], vl[1]);
+    e2m1_pair<2>(d, vh[2], vl[2]);
+    e2m1_pair<3>(d, vh[3], vl[3]);
+  } else {
+    // NF4 LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
+    // byte b hold its high code (the first element); after a left shift by
+    // 3, its low code.
+    const uint32_t dh = d >> 1;
+    const uint32_t dl = d << 3;
+    uint32_t oh[4], ol[4];
+    oh[0] = byte_and<0>(dh, 0x78u);
+    oh[1] = byte_and<1>(dh, 0x78u);
+    oh[2] = byte_and<2>(dh, 0x78u);
+    oh[3] = byte_and<3>(dh, 0x78u);
+    ol[0] = byte_and<0>(dl, 0x78u);
+    ol[1] = byte_and<1>(dl, 0x78u);
+    ol[2] = byte_and<2>(dl, 0x78u);
+    ol[3] = byte_and<3>(dl, 0x78u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      vh[b] = lut_at(lut, oh[b]);
+      vl[b] = lut_at(lut, ol[b]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      pr[r] = fmaf(xw[r][2 * b], vh[b], pr[r]);
+      pr[r] = fmaf(xw[r][2 * b + 1], vl[b], pr[r]);
+    }
+  }
 }
 
 // One group, one K split, a tile of weight rows; activation rows in chunks
@@ -330,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 
   // (2) + (3): the first chunk's activations, then every weight chunk
   rows_of(r_begin);
-  XStage<R> stage;
+  XStage<R, x_batch(R, L, STEPS)> stage;
   stage.init(c_begin, ncs);
   stage.load(a.g.x, K, xrow, 0);
   uint4 wq[STEPS][NU];
@@ -341,19 +399,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     load_weights<NU, AbsT>(wexp, aexp, row_bytes, bpr, N, n_base, c, c < c_end, wq[st], av[st]);
   }
   stage.store(s_x, 0);
-  for (int base = kXBatch * kThreads; base < R * stage.per_row; base += kXBatch * kThreads) {
-    stage.load(a.g.x, K, xrow, base);
-    stage.store(s_x, base);
-  }
 
-  for (int r0 = r_begin; r0 < r_end; r0 += R) {
-    if (r0 != r_begin) {
-      lds_barrier();  // every wavefront is done with the previous chunk
-      rows_of(r0);
-      stage.all(a.g.x, K, xrow, s_x);
-    }
-    lds_barrier();
-
+  // One chunk of R activation rows against the lane's weights, after the
+  // barrier that publishes the chunk's staged activations.
+  auto chunk = [&](int r0) {
     float acc[NU][R];
 #pragma unroll
     for (int j = 0; j < NU; ++j)
@@ -369,10 +418,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
       for (int j = 0; j < NU; ++j)
 #pragma unroll
         for (int r = 0; r < R; ++r) pr[j][r] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // the 8 activations of weight dword w, shared by the NU rows
-        float xw[R][8];
+      // the 8 activations of weight dword w of this chunk, R rows
+      auto x_of = [&](int w, float (&xw)[R][8]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float4* src = s_x + (r * 8 + 2 * w) * plane + (c - c_begin);
@@ -380,47 +427,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
           xw[r][0] = lo.x; xw[r][1] = lo.y; xw[r][2] = lo.z; xw[r][3] = lo.w;
           xw[r][4] = hi.x; xw[r][5] = hi.y; xw[r][6] = hi.z; xw[r][7] = hi.w;
         }
+      };
+      // The empty asm pins each dword's first use here: hoisted out of the
+      // row-chunk loop, the decode of every row would wait for every load.
+      auto dword_of = [&](int j, int w) -> uint32_t {
+        uint32_t d = w == 0 ? wq[st][j].x : w == 1 ? wq[st][j].y : w == 2 ? wq[st][j].z : wq[st][j].w;
+        asm volatile("" : "+v"(d));
+        return d;
+      };
+      if constexpr (R == 1 && NU > 1) {
+        // Row by row: row j's terms need only row j's load, so the decode
+        // of the first rows runs while the later rows are still arriving.
+        float xw[4][R][8];
 #pragma unroll
-        for (int j = 0; j < NU; ++j) {
-          const uint32_t d = w == 0 ? wq[st][j].x : w == 1 ? wq[st][j].y
-                           : w == 2 ? wq[st][j].z : wq[st][j].w;
-          // the two elements of each byte: vh the first, vl the second
-          float vh[4], vl[4];
-          if constexpr (kMxfp4<AbsT>) {
-            // E2M1 through the hardware convert (first element = low nibble)
-            e2m1_pair<0>(d, vh[0], vl[0]);
-            e2m1_pair<1>(d, vh[1], vl[1]);
-            e2m1_pair<2>(d, vh[2], vl[2]);
-            e2m1_pair<3>(d, vh[3], vl[3]);
-          } else {
-            // NF4 LUT byte offsets 8 * code: after a right shift by 1, bits
-            // 3..6 of byte b hold its high code (the first element); after a
-            // left shift by 3, its low code.
-            const uint32_t dh = d >> 1;
-            const uint32_t dl = d << 3;
-            uint32_t oh[4], ol[4];
-            oh[0] = byte_and<0>(dh, 0x78u);
-            oh[1] = byte_and<1>(dh, 0x78u);
-            oh[2] = byte_and<2>(dh, 0x78u);
-            oh[3] = byte_and<3>(dh, 0x78u);
-            ol[0] = byte_and<0>(dl, 0x78u);
-            ol[1] = byte_and<1>(dl, 0x78u);
-            ol[2] = byte_and<2>(dl, 0x78u);
-            ol[3] = byte_and<3>(dl, 0x78u);
+        for (int w = 0; w < 4; ++w) x_of(w, xw[w]);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              vh[b] = lut_at(lut, oh[b]);
-              vl[b] = lut_at(lut, ol[b]);
-            }
-          }
+        for (int j = 0; j < NU; ++j)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
+          for (int w = 0; w < 4; ++w) dword_terms<R, AbsT>(dword_of(j, w), xw[w], lut, pr[j]);
+      } else {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-              pr[j][r] = fmaf(xw[r][2 * b], vh[b], pr[j][r]);
-              pr[j][r] = fmaf(xw[r][2 * b + 1], vl[b], pr[j][r]);
-            }
-          }
+        for (int w = 0; w < 4; ++w) {
+          float xw[R][8];  // shared by the NU rows
+          x_of(w, xw);
+#pragma unroll
+          for (int j = 0; j < NU; ++j) dword_terms<R, AbsT>(dword_of(j, w), xw, lut, pr[j]);
         }
       }
 #pragma unroll
@@ -449,6 +480,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
           a.g.partial[((size_t)s * a.g.M + row) * N + n] = acc[j][r];
       }
     }
+  };
+
+  // The first chunk outside the loop: a loop around it, with the staging
+  // loads of later chunks, would make the compiler wait for every weight
+  // load before the first row's decode.
+  lds_barrier();
+  chunk(r_begin);
+  for (int r0 = r_begin + R; r0 < r_end; r0 += R) {
+    lds_barrier();  // every wavefront is done with the previous chunk
+    rows_of(r0);
+    stage.all(a.g.x, K, xrow, s_x);
+    lds_barrier();
+    chunk(r0);
   }
 }
 
@@ -476,6 +520,10 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
 
 template <int L, int NU, int R, int STEPS, typename AbsT, bool ROUTED = false>
 hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  // one staging round must cover the split's activation rows
+  if (p.L != L || p.steps != STEPS || p.R != R || p.cps > L * STEPS ||
+      R * (p.cps + 1) > kXSlots)
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)p.n_tiles, (unsigned)group_slots(a.g.G, a.g.M, 1), (unsigned)p.S);
   const size_t lds = (size_t)R * (size_t)(p.cps + 1) * 128;
   hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS, AbsT, ROUTED>), grid, dim3(kThreads), lds,
