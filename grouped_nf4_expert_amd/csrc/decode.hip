@@ -599,13 +599,15 @@ int pick_lanes(int cps) {
 // group; for each K split S (1 first, more only while a split keeps two team
 // steps per lane) the team width L and steps follow from the split's chunks,
 // and the rows per lane NU is the largest with NU * steps <= 4 and
-// NU * R <= 4 that still gives two wavefronts per SIMD; a split must fit its
-// activations in LDS.
+// NU * R <= 4 that gives four wavefronts per SIMD, else the largest that
+// gives two (a split is taken only when no NU of the smaller one gives
+// two); a split must fit its activations in LDS.
 static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, int split_k,
                                    int num_cus) {
   const int cpr = (int)(K / 32);
   const int64_t g_eff = G < M ? G : M;
-  const int64_t target_waves = 8LL * num_cus;  // two per SIMD
+  const int64_t min_waves = 8LL * num_cus;    // two per SIMD
+  const int64_t good_waves = 16LL * num_cus;  // four per SIMD
   const double rows_per_group = (double)M / (double)(g_eff > 0 ? g_eff : 1);
   const int R0 = rows_per_group <= 1.5 ? 1 : (rows_per_group <= 3.0 ? 2 : 4);
   for (int R = R0; R >= 1; R /= 2) {
@@ -621,6 +623,8 @@ static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, i
       if (split_more && cps < 2 * L) break;
       split_more = true;
       const int steps = (cps + L - 1) / L;
+      DecodePlan enough{};  // the largest NU reaching min_waves
+      bool have_enough = false;
       for (int NU = kMaxLoads; NU >= 1; NU /= 2) {
         if (NU * steps > kMaxLoads || NU * R > kMaxLoads) continue;
         DecodePlan p{};
@@ -633,12 +637,17 @@ static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, i
         p.rows_per_block = kWaves * (kWave / L) * NU;
         p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
         const int64_t waves = g_eff * p.n_tiles * S * kWaves;
-        if (waves >= target_waves) return p;
+        if (waves >= good_waves) return p;
+        if (waves >= min_waves && !have_enough) {
+          enough = p;
+          have_enough = true;
+        }
         if (waves > best_waves) {
           best_waves = waves;
           best = p;
         }
       }
+      if (have_enough) return enough;
     }
     if (best_waves >= 0) return best;
   }
