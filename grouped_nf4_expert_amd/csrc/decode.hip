@@ -511,9 +511,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
       const int slot = a.g.slots[r];
       if (slot < 0 || slot >= a.g.T * a.g.slot_div) continue;
     }
-    const float* p = a.g.partial + (size_t)r * a.g.N + n;
-    float sum = 0.0f;
-    for (int si = 0; si < a.S; ++si) sum += p[si * plane];
+    const float sum = sum_splits(a.g.partial + (size_t)r * a.g.N + n, plane, a.S);
     a.g.y[(size_t)r * a.g.N + n] = f32_to_bf16(sum);
   }
 }

@@ -170,9 +170,7 @@ __global__ __launch_bounds__(256) void dgrad_reduce_kernel(DgradKArgs a) {
   const int r_end = min(gr.row + gr.size, a.M);
   const size_t plane = (size_t)a.M * a.K;
   for (int r = gr.row; r < r_end; ++r) {
-    const float* p = a.partial + (size_t)r * a.K + k;
-    float sum = 0.0f;
-    for (int si = 0; si < a.S; ++si) sum += p[si * plane];
+    const float sum = sum_splits(a.partial + (size_t)r * a.K + k, plane, a.S);
     a.dx[(size_t)r * a.K + k] = f32_to_bf16(sum);
   }
 }

@@ -52,6 +52,27 @@ __device__ __forceinline__ float absmax_at(const uint16_t* p, size_t i) {
   return bf16_to_f32(p[i]);
 }
 
+// p[0] + p[plane] + ... + p[(S - 1) * plane] added in split order, starting
+// from +0, with up to 16 loads in flight (one per split, each a memory round
+// trip).  Every load is issued, clamped to the last split; the padding adds
+// +0, which leaves the sum unchanged (a sum started at +0 is never -0).
+__device__ __forceinline__ float sum_splits(const float* p, size_t plane, int S) {
+  constexpr int kBatch = 16;
+  float sum = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int si = min(s0 + u, S - 1);
+      const float t = p[(size_t)si * plane];
+      v[u] = s0 + u < S ? t : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) sum += v[u];
+  }
+  return sum;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
