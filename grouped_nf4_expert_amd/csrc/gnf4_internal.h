@@ -189,7 +189,7 @@ hipError_t launch_pack(const void* w, int dtype, int64_t n_blocks, uint8_t* pack
 
 struct RoutePlan {
   int chunk_tokens;   // tokens per chunk of the sort
-  int n_chunks;       // 1 => single fused launch
+  int n_chunks;       // 0 => single fused launch (T <= 32)
   size_t ws_bytes;    // per-chunk counts
 };
 RoutePlan plan_route(int64_t T, int64_t E, int top_k);

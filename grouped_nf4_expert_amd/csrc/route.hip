@@ -17,14 +17,15 @@
 //  * a single token (every batch-1 decode step) needs no sort at all: its
 //    picks are distinct experts, so each pick's place in expert order is a
 //    ballot prefix count; one wavefront writes every output.
-//  * more tokens: a counting sort by expert over chunks of 64 tokens.  Per
+//  * more tokens: a counting sort by expert over chunks of tokens.  Per
 //    chunk an LDS histogram (counts commute, so LDS atomics are safe); an
 //    exclusive scan over (expert, chunk) gives every chunk's first row per
 //    expert; one wavefront per chunk then walks its slots in ascending order,
 //    ranking equal experts inside each 64-slot batch with ballots, so the
-//    output is the stable order.  One chunk runs as ONE launch (16
+//    output is the stable order.  Up to 32 tokens run as ONE launch (16
 //    wavefronts); larger batches use three (top-k + histogram, scan,
-//    scatter).
+//    scatter) over chunks of 16 tokens, one per wavefront of a 16-wavefront
+//    workgroup, so a batch of T tokens spreads over T / 16 workgroups.
 
 #include <math.h>
 
@@ -36,7 +37,8 @@ namespace {
 
 constexpr int kRouteThreads = 1024;  // 16 wavefronts: one token each at a time
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kChunkTokens = 64;
+constexpr int kFusedTokens = 32;  // the single-launch sort takes up to this many tokens
+constexpr int kChunkTokens = 16;  // tokens per chunk of the three-launch sort
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 
@@ -182,7 +184,7 @@ __device__ void scatter_slots(const int32_t* ids, int s0, int s1, int32_t* base,
 // Whole sort in one workgroup: T * K fits one chunk.
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a) {
-  __shared__ int32_t s_ids[kChunkTokens * kMaxK];
+  __shared__ int32_t s_ids[kFusedTokens * kMaxK];
   __shared__ int32_t s_cnt[kMaxE];
   __shared__ int32_t s_base[kMaxE];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -223,26 +225,63 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_hist_kernel(RouteArg
 
 // Large batches, step 2 (one workgroup of 1024): per-expert totals, the scan,
 // the groups, and every chunk's base row per expert (in place of its count).
+// Q = 1024 / E' threads per expert (E' is E rounded up to a power of two,
+// at least 64, so Q is 16, 8, 4, 2 or 1) each take a contiguous range of the
+// chunks with up to 16 count loads in flight: pass 1 sums the range, pass 2
+// writes the bases after the expert scan.
 __global__ __launch_bounds__(1024) void route_scan_kernel(RouteArgs a) {
   __shared__ int32_t s_tot[kMaxE];
   __shared__ int32_t s_base[kMaxE];
-  const int e = threadIdx.x;
-  if (e < a.E) {
-    int run = 0;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      int32_t* p = a.ws + (size_t)c * a.E + e;
-      const int cnt = *p;
-      *p = run;
-      run += cnt;
+  __shared__ int32_t s_part[1024];
+  constexpr int kB = 16;
+  int ep = kWave;
+  while (ep < a.E) ep *= 2;
+  const int Q = 1024 / ep;
+  const int e = threadIdx.x % ep, q = threadIdx.x / ep;
+  const int per = (a.n_chunks + Q - 1) / Q;
+  const int c_begin = min(q * per, a.n_chunks);
+  const int c_end = min(c_begin + per, a.n_chunks);
+  const bool mine = e < a.E;
+  int32_t* col = a.ws + (mine ? e : 0);  // column e of the [n_chunks, E] counts
+  // pass 1: this thread's share of expert e's count
+  int part = 0;
+  if (mine) {
+    for (int c0 = c_begin; c0 < c_end; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int t = col[(size_t)min(c0 + u, c_end - 1) * a.E];
+        v[u] = c0 + u < c_end ? t : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) part += v[u];
     }
+  }
+  s_part[threadIdx.x] = part;
+  __syncthreads();
+  if (threadIdx.x < ep && mine) {
+    int run = 0;
+    for (int qq = 0; qq < Q; ++qq) run += s_part[qq * ep + e];
     s_tot[e] = run;
   }
   __syncthreads();
   if (threadIdx.x < kWave) scan_and_groups(s_tot, s_base, a, threadIdx.x);
   __syncthreads();
-  if (e < a.E) {
-    const int b = s_base[e];
-    for (int c = 0; c < a.n_chunks; ++c) a.ws[(size_t)c * a.E + e] += b;
+  if (!mine) return;
+  // pass 2: the base row of every chunk in the range
+  int run = s_base[e];
+  for (int qq = 0; qq < q; ++qq) run += s_part[qq * ep + e];
+  for (int c0 = c_begin; c0 < c_end; c0 += kB) {
+    int v[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) v[u] = col[(size_t)min(c0 + u, c_end - 1) * a.E];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (c0 + u < c_end) {
+        col[(size_t)(c0 + u) * a.E] = run;
+        run += v[u];
+      }
+    }
   }
 }
 
@@ -273,7 +312,7 @@ template <int EPL>
 void launch_epl(const RouteArgs& a, const RoutePlan& plan, hipStream_t stream) {
   if (a.T == 1) {
     hipLaunchKernelGGL(route_one_token_kernel<EPL>, dim3(1), dim3(kWave), 0, stream, a);
-  } else if (plan.n_chunks == 1) {
+  } else if (plan.n_chunks == 0) {
     hipLaunchKernelGGL(route_fused_kernel<EPL>, dim3(1), dim3(kRouteThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(route_topk_hist_kernel<EPL>, dim3(plan.n_chunks), dim3(kRouteThreads), 0,
@@ -288,8 +327,8 @@ void launch_epl(const RouteArgs& a, const RoutePlan& plan, hipStream_t stream) {
 RoutePlan plan_route(int64_t T, int64_t E, int top_k) {
   RoutePlan p;
   p.chunk_tokens = kChunkTokens;
-  p.n_chunks = (int)((T + kChunkTokens - 1) / kChunkTokens);
-  p.ws_bytes = p.n_chunks > 1 ? (size_t)p.n_chunks * (size_t)E * sizeof(int32_t) : 0;
+  p.n_chunks = T <= kFusedTokens ? 0 : (int)((T + kChunkTokens - 1) / kChunkTokens);
+  p.ws_bytes = (size_t)p.n_chunks * (size_t)E * sizeof(int32_t);
   (void)top_k;
   return p;
 }

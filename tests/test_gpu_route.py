@@ -38,9 +38,9 @@ def test_route_workloads(name):
     _run_and_compare(wls.router_logits(wl), wl.top_k, name)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 2, 2), (64, 64, 8), (65, 64, 8),
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 2, 2), (32, 64, 8), (33, 64, 8), (64, 64, 8), (65, 64, 8),
                                    (129, 128, 4), (7, 1024, 32), (300, 1024, 32),
-                                   (1000, 256, 8)])
+                                   (1000, 256, 8), (2000, 96, 6), (1500, 512, 16)])
 def test_route_shapes(T, E, k):
     rng = np.random.default_rng(T * 7 + E)
     _run_and_compare(rng.standard_normal((T, E)).astype(np.float32), k, "shape")
