@@ -14,6 +14,9 @@
 //    dy[r, n] * absmax, computed once per row and block;
 //  * the 8 wavefronts of a workgroup cover disjoint row slices; their
 //    partial sums meet in LDS and are added in wavefront order;
+//  * at one row of dy per pass (groups of about one row) every row has its
+//    own workgroup slot, so the rows of a larger group run side by side
+//    instead of as passes one after another;
 //  * when N is split across workgroups to fill the machine, each split
 //    writes fp32 partials that a second kernel sums in split order, so the
 //    result is deterministic run to run.
@@ -62,8 +65,19 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
   __shared__ float s_red[kWaves * kWave * kChunkPitch];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // R == 1: one workgroup slot per row, so the rows of a group run side by
+  // side instead of one pass after another; otherwise one slot per group.
   GroupRef gr;
-  if (!find_group(a.sizes, a.ids, a.G, a.E, a.M, 1, INT_MAX, blockIdx.y, gr)) return;
+  int r_begin, r_end;
+  if constexpr (R == 1) {
+    if (!find_row_group(a.sizes, a.ids, a.G, a.E, a.M, blockIdx.y, gr)) return;
+    r_begin = blockIdx.y;
+    r_end = r_begin + 1;
+  } else {
+    if (!find_group(a.sizes, a.ids, a.G, a.E, a.M, 1, INT_MAX, blockIdx.y, gr)) return;
+    r_begin = gr.row;
+    r_end = min(r_begin + gr.size, a.M);
+  }
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const int N = a.N, K = a.K;
   const int cpr = K / 32;                     // 16-byte chunks per weight row
@@ -77,8 +91,6 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   const int s = blockIdx.z;
   const int n_begin = s * a.rows_per_split;
   const int n_end = min(n_begin + a.rows_per_split, N);
-  const int r_begin = gr.row;
-  const int r_end = min(r_begin + gr.size, a.M);
 
   for (int r0 = r_begin; r0 < r_end; r0 += R) {
     float acc[R][32];
@@ -217,7 +229,7 @@ hipError_t launch_dgrad(const DgradArgs& g, const DgradPlan& p, hipStream_t stre
   a.M = g.M;
   a.S = p.S;
   a.rows_per_split = p.rows_per_split;
-  const unsigned slots = (unsigned)group_slots(g.G, g.M, 1);
+  const unsigned slots = (unsigned)(p.R == 1 ? g.M : group_slots(g.G, g.M, 1));
   if (slots == 0) return hipSuccess;
   const dim3 grid((unsigned)p.k_tiles, slots, (unsigned)p.S);
   if (g.abs_bf16) {
