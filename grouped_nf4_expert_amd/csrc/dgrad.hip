@@ -60,6 +60,50 @@ __device__ __forceinline__ float lut_at(const float* lut16, uint32_t byte_off) {
   return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut16) + byte_off);
 }
 
+// The group holding row j (0 <= j < M) when its expert id lies in [0, E):
+// the group g with row(g) <= j < row(g) + size(g), sizes clamped to [0, M]
+// and summed in group order as find_group does.  False when row j belongs to
+// no group (past the sum of the sizes) or to one with an invalid expert id.
+// Call with the whole wavefront active; every lane gets the same result.
+// A wavefront's partial sums fit an int (M < 2^25); the running row count is
+// 64-bit, so sizes summing far past M cannot wrap it.
+__device__ __forceinline__ bool find_row_group(const int32_t* sizes, const int32_t* ids, int G,
+                                               int E, int M, int j, GroupRef& out) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  long long rows = 0;
+  for (int c0 = 0; c0 < G; c0 += 4 * kWave) {
+    int sv[4], ev[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = c0 + q * kWave + lane;
+      sv[q] = i < G ? min(max(sizes[i], 0), M) : 0;
+      ev[q] = i < G ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int incl = wave_incl_scan(sv[q]);
+      // the lane whose rows [end - size, end) hold j; the non-empty groups'
+      // ranges tile the rows, so exactly one lane hits when j is in this batch
+      const long long end = rows + incl;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(sv[q] > 0 && end - sv[q] <= j && j < end);
+      if (m) {
+        const int src = __builtin_ctzll(m);
+        const int ex = __builtin_amdgcn_readlane(ev[q], src);
+        if (ex < 0 || ex >= E) return false;
+        const int sz = __builtin_amdgcn_readlane(sv[q], src);
+        out.g = c0 + q * kWave + src;
+        out.size = sz;
+        out.expert = ex;
+        out.row = (int)(rows + __builtin_amdgcn_readlane(incl, src) - sz);
+        return true;
+      }
+      rows += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (rows > j) return false;
+  }
+  return false;
+}
+
 template <int R, typename AbsT>
 __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
