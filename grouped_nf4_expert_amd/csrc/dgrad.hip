@@ -5,10 +5,12 @@
 // dgrad.  The contraction runs over N, across the rows of the K-contiguous
 // [N, K/2] codes, so the access is the transpose of the forward GEMM's:
 //  * a lane owns one 16-byte chunk (32 consecutive k) of the weight rows and
-//    accumulates those 32 outputs in fp32 for up to R rows of dy; its
-//    wavefront walks a slice of the N rows, 8 rows in flight at a time
-//    (16-byte code loads coalesced across the 64 lanes of a row, the block
-//    absmax, and dy[r, n], the same for the whole wavefront);
+//    accumulates those 32 outputs in fp32 for up to R rows of dy; a team of
+//    L lanes (64, 32, 16 or 8, from K, so few lanes sit past the row's end)
+//    covers L consecutive chunks, and the 64 / L teams of a wavefront walk
+//    different rows of a slice of N, 8 rows per team in flight at a time
+//    (16-byte code loads coalesced across the team, the block absmax, and
+//    dy[r, n], the same for the whole team);
 //  * each code is decoded through a 16-entry fp32 table in LDS at an 8-byte
 //    stride (conflict-free for any mix of codes) and multiplied-added with
 //    dy[r, n] * absmax, computed once per row and block;
@@ -104,11 +106,15 @@ __device__ __forceinline__ bool find_row_group(const int32_t* sizes, const int32
   return false;
 }
 
-template <int R, typename AbsT>
+// L lanes (a team) cover L consecutive chunks of a weight row; the 64 / L
+// teams of a wavefront take different weight rows.
+template <int L, int R, typename AbsT>
 __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
+  constexpr int RPW = kWave / L;  // teams per wavefront
   __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
   __shared__ float s_red[kWaves * kWave * kChunkPitch];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int team = lane / L, tl = lane % L;
   // R == 1: one workgroup slot per row, so the rows of a group run side by
   // side instead of one pass after another; otherwise one slot per group.
   GroupRef gr;
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const int N = a.N, K = a.K;
   const int cpr = K / 32;                     // 16-byte chunks per weight row
-  const int c = blockIdx.x * kWave + lane;    // this lane's chunk
+  const int c = blockIdx.x * L + tl;          // this lane's chunk
   const bool c_ok = c < cpr;
   const int cc = c_ok ? c : 0;
   const int bpr = K / kBlock;
@@ -142,32 +148,45 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < 32; ++j) acc[r][j] = 0.0f;
-    // this wavefront's rows: n_begin + wave + kWaves * i
-    for (int n0 = n_begin + wave; n0 < n_end; n0 += kWaves * kNB) {
+    // this lane's rows: n_begin + (wave * RPW + team) + kWaves * RPW * i
+    for (int n0 = n_begin + wave * RPW; n0 < n_end; n0 += kWaves * RPW * kNB) {
+      // Every load is issued, from a clamped (existing) row, chunk and dy row,
+      // and what does not exist is zeroed where it is used: loads in
+      // branches would make the compiler wait for all of them before the
+      // first row's terms.
       uint4 wq[kNB];
       float av[kNB];
       float dv[kNB][R];
+      bool live[kNB];
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
-        const int n = n0 + kWaves * b;
+        const int n = n0 + team + kWaves * RPW * b;
         const bool ok = n < n_end;
         const int nn = ok ? n : n_begin;
+        live[b] = ok && c_ok;
         wq[b] = *reinterpret_cast<const uint4*>(wexp + (size_t)nn * row_bytes + 16 * (size_t)cc);
-        av[b] = (ok && c_ok) ? absmax_at(aexp, (size_t)nn * bpr + (cc >> 1)) : 0.0f;
+        av[b] = absmax_at(aexp, (size_t)nn * bpr + (cc >> 1));
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int row = min(r0 + r, r_end - 1);
-          dv[b][r] = (r0 + r < r_end) ? bf16_to_f32(a.dy[(size_t)row * N + nn]) : 0.0f;
-        }
+        for (int r = 0; r < R; ++r)
+          dv[b][r] = bf16_to_f32(a.dy[(size_t)min(r0 + r, r_end - 1) * N + nn]);
       }
+      // The empty asms pin each loaded value's first use to its row's terms,
+      // so row b waits only for its own loads.
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
+        float ab = av[b];
+        asm volatile("" : "+v"(ab));
         float sc[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) sc[r] = dv[b][r] * av[b];
+        for (int r = 0; r < R; ++r) {
+          float db = dv[b][r];
+          asm volatile("" : "+v"(db));
+          sc[r] = (live[b] && r0 + r < r_end) ? db * ab : 0.0f;
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t d = w == 0 ? wq[b].x : w == 1 ? wq[b].y : w == 2 ? wq[b].z : wq[b].w;
+          uint32_t d = w == 0 ? wq[b].x : w == 1 ? wq[b].y : w == 2 ? wq[b].z : wq[b].w;
+          asm volatile("" : "+v"(d));
           // LUT byte offsets 8 * code: after a right shift by 1, bits 3..6 of
           // byte q hold its high code; after a left shift by 3, its low code
           const uint32_t dh = d >> 1, dl = d << 3;
@@ -188,8 +207,9 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
         }
       }
     }
-    // wavefront partials meet in LDS; thread t sums outputs t, t + 512, ...
-    // over the wavefronts in order
+    // team partials meet in LDS; thread t sums outputs t, t + 512, ... of
+    // the tile's L * 32 over the wavefronts in order, and over the teams in
+    // order within each
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       __syncthreads();  // the previous row's readers are done
@@ -200,13 +220,16 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
       const int row = r0 + r;
       if (row >= r_end) continue;
 #pragma unroll
-      for (int q = 0; q < (kWave * 32) / kThreads; ++q) {
-        const int p = threadIdx.x + kThreads * q;  // position in the tile: lane p / 32, k p % 32
+      for (int q = 0; q < (L * 32 + kThreads - 1) / kThreads; ++q) {
+        const int p = threadIdx.x + kThreads * q;  // position in the tile: chunk p / 32, k p % 32
+        if (p >= L * 32) continue;
         const int pl = p >> 5, pj = p & 31;
-        const int k = 32 * (blockIdx.x * kWave + pl) + pj;
+        const int k = 32 * (blockIdx.x * L + pl) + pj;
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += s_red[(w * kWave + pl) * kChunkPitch + pj];
+        for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+          for (int t = 0; t < RPW; ++t) sum += s_red[(w * kWave + t * L + pl) * kChunkPitch + pj];
         if (k >= K) continue;
         if (a.S == 1)
           a.dx[(size_t)row * K + k] = f32_to_bf16(sum);
@@ -233,24 +256,66 @@ __global__ __launch_bounds__(256) void dgrad_reduce_kernel(DgradKArgs a) {
 
 }  // namespace
 
-// Launch rule (host-known sizes only): R from the rows per group; N split so
-// the grid holds about two wavefronts per SIMD, each split at least one
-// batch of rows per wavefront.
+// Team width for rows of cpr chunks: the widest of 64/32/16/8 lanes whose
+// tiles leave less than half of the chunk slots idle, else the one with the
+// least idle share.  (Narrower teams mean more tiles and more rows per
+// workgroup pass: GPT-OSS's 90 chunks ran faster on two 64-lane tiles, 30%
+// idle, than on three 32-lane ones; OLMoE's 32 chunks faster on 32 lanes.)
+static int dgrad_lanes(int64_t cpr) {
+  const int cands[4] = {64, 32, 16, 8};
+  int best = 64;
+  double best_waste = 2.0;
+  for (int L : cands) {
+    const int64_t tiles = (cpr + L - 1) / L;
+    const double waste = (double)(tiles * L - cpr) / (double)(tiles * L);
+    if (waste < 0.5) return L;
+    if (waste < best_waste) {
+      best_waste = waste;
+      best = L;
+    }
+  }
+  return best;
+}
+
+// Launch rule (host-known sizes only): R from the rows per group; the team
+// width L from K; N split so the grid holds about two wavefronts per SIMD,
+// each split at least one batch of rows per team.
 DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
   DgradPlan p;
   const int64_t g_eff = G < M ? G : M;
   const double rows_per_group = (double)M / (double)(g_eff > 0 ? g_eff : 1);
   p.R = rows_per_group <= 1.5 ? 1 : (rows_per_group <= 3.0 ? 2 : 4);
-  p.k_tiles = (int)((K / 32 + kWave - 1) / kWave);
+  const int64_t cpr = K / 32;
+  p.L = dgrad_lanes(cpr);
+  p.k_tiles = (int)((cpr + p.L - 1) / p.L);
+  const int64_t rows_per_batch = (int64_t)kWaves * (kWave / p.L) * kNB;
   const int64_t target_waves = 8LL * num_cus;
   const int64_t per_split = (g_eff > 0 ? g_eff : 1) * p.k_tiles * kWaves;
   int64_t S = (target_waves + per_split - 1) / per_split;
-  const int64_t max_s = (N + kWaves * kNB - 1) / (kWaves * kNB);
+  const int64_t max_s = (N + rows_per_batch - 1) / rows_per_batch;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
   p.rows_per_split = (int)((N + S - 1) / S);
   p.S = (int)((N + p.rows_per_split - 1) / p.rows_per_split);
   return p;
+}
+
+template <int L>
+static void launch_dgrad_L(const DgradKArgs& a, bool abs_bf16, int R, dim3 grid,
+                           hipStream_t stream) {
+  if (abs_bf16) {
+    switch (R) {
+      case 1: hipLaunchKernelGGL((dgrad_kernel<L, 1, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((dgrad_kernel<L, 2, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((dgrad_kernel<L, 4, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+  } else {
+    switch (R) {
+      case 1: hipLaunchKernelGGL((dgrad_kernel<L, 1, float>), grid, dim3(kThreads), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((dgrad_kernel<L, 2, float>), grid, dim3(kThreads), 0, stream, a); break;
+      default: hipLaunchKernelGGL((dgrad_kernel<L, 4, float>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+  }
 }
 
 size_t dgrad_workspace_bytes(const DgradPlan& p, int64_t M, int64_t K) {
@@ -276,18 +341,12 @@ hipError_t launch_dgrad(const DgradArgs& g, const DgradPlan& p, hipStream_t stre
   const unsigned slots = (unsigned)(p.R == 1 ? g.M : group_slots(g.G, g.M, 1));
   if (slots == 0) return hipSuccess;
   const dim3 grid((unsigned)p.k_tiles, slots, (unsigned)p.S);
-  if (g.abs_bf16) {
-    switch (p.R) {
-      case 1: hipLaunchKernelGGL((dgrad_kernel<1, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((dgrad_kernel<2, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((dgrad_kernel<4, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-    }
-  } else {
-    switch (p.R) {
-      case 1: hipLaunchKernelGGL((dgrad_kernel<1, float>), grid, dim3(kThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((dgrad_kernel<2, float>), grid, dim3(kThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((dgrad_kernel<4, float>), grid, dim3(kThreads), 0, stream, a); break;
-    }
+  switch (p.L) {
+    case 64: launch_dgrad_L<64>(a, g.abs_bf16, p.R, grid, stream); break;
+    case 32: launch_dgrad_L<32>(a, g.abs_bf16, p.R, grid, stream); break;
+    case 16: launch_dgrad_L<16>(a, g.abs_bf16, p.R, grid, stream); break;
+    case 8: launch_dgrad_L<8>(a, g.abs_bf16, p.R, grid, stream); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;

@@ -255,7 +255,8 @@ struct DgradArgs {
 
 struct DgradPlan {
   int R;               // rows of dy per pass over the weights
-  int k_tiles;         // 2048-wide slices of K (one chunk per lane)
+  int L;               // lanes per weight row (a team); 64 / L teams per wavefront
+  int k_tiles;         // slices of K of L chunks of 32 (one chunk per lane)
   int S;               // N splits
   int rows_per_split;  // weight rows per split
 };
