@@ -103,6 +103,21 @@ def test_dgrad_boundaries(case, path):
         check_gemm(dx, c["o"], c["written"], f"dgrad {case} path {path}")
 
 
+# Rows of 10, 16, 24 and 32 chunks of 32 codes: the decode path's teams of
+# 16, 16, 32 and 32 lanes (several weight rows per wavefront), with groups of
+# one row (one workgroup slot per row) and of several rows (R > 1, and groups
+# whose rows take separate slots).
+@pytest.mark.parametrize("K", [320, 512, 768, 1024])
+@pytest.mark.parametrize("sizes,ids,M", [([1, 1, 1, 1], [3, 0, 2, 1], 4),
+                                         ([1, 3, 2, 1], [2, 0, 3, 1], 7),
+                                         ([5, 3], [1, 2], 8)])
+def test_dgrad_team_widths(K, sizes, ids, M):
+    note(f"dgrad team widths K={K} sizes={sizes}")
+    c = _custom(4, 200, K, sizes, ids, M, seed=K + M)
+    dx = _run(c, path=DEC)
+    check_gemm(dx, c["o"], c["written"], f"dgrad K={K} sizes={sizes}")
+
+
 def _absmax_scenarios(E, N, K):
     """Weight magnitudes that stress the tile path's per-column-block scale:
     blocks alternating 1e-30 / 1e30 along K, one row 1e4 above the others,
