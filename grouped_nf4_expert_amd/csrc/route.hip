@@ -10,10 +10,12 @@
 //  * top-k by rank: each logit becomes a unique 64-bit key (order-preserving
 //    float key in the high half, the complement of the expert id in the low
 //    half: larger = better, equal logits go to the lower id).  One
-//    wavefront per token; a lane ranks each of its keys against every key of
-//    the token (broadcast with readlane) -- independent compare-adds instead
-//    of k dependent arg-max rounds -- and the keys ranked below k are the
-//    picks, in order.  Weights are the softmax of the k picks in fp32.
+//    wavefront per token.  Up to 64 experts a lane ranks its key against
+//    every key of the token (broadcast with readlane) -- independent
+//    compare-adds instead of k dependent arg-max rounds; above 64, the k-th
+//    largest key is found bit by bit from ballot counts and only the k picks
+//    are ranked against each other.  The keys ranked below k are the picks,
+//    in order.  Weights are the softmax of the k picks in fp32.
 //  * a single token (every batch-1 decode step) needs no sort at all: its
 //    picks are distinct experts, so each pick's place in expert order is a
 //    ballot prefix count; one wavefront writes every output.
@@ -57,6 +59,63 @@ struct RouteArgs {
   int n_chunks;
 };
 
+// Ranks of one token's k picks for E > 64, by threshold: the k-th largest
+// key T is built bit by bit from the top, a bit kept when at least k keys
+// are >= the candidate (ballot counts); the keys >= T are the k picks, and a
+// pick's rank is the number of picks above it (non-picks get rank k).  The
+// keys are rank_token's (float key, then the complement of the expert id;
+// absent entries 0, below every real key), so the picks, their order and the
+// ties are the same.  A real key's low word is 0xffffffff - e with e < 1024,
+// so once the high word of T is known its bits 31..10 are all ones.
+template <int EPL>
+__device__ __forceinline__ void rank_picks(const float* __restrict__ row, int E, int k, int lane,
+                                           float (&val)[EPL], int (&rank)[EPL]) {
+  uint32_t hi[EPL];
+  uint64_t key[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const int e = lane + kWave * s;
+    val[s] = (e < E) ? row[e] : 0.0f;
+    hi[s] = (e < E) ? float_key(val[s]) : 0u;
+    key[s] = (e < E) ? (((uint64_t)hi[s] << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+  }
+  // the high word of T: the k-th largest float key, counting equal ones
+  uint32_t th = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = th | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) cnt += __popcll(__ballot(hi[s] >= cand));
+    if (cnt >= k) th = cand;
+  }
+  // the low word: bits 31..10 are ones; bits 9..0 pick among equal logits
+  uint64_t t = ((uint64_t)th << 32) | 0xfffffc00u;
+  for (int b = 9; b >= 0; --b) {
+    const uint64_t cand = t | (1ull << b);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) cnt += __popcll(__ballot(key[s] >= cand));
+    if (cnt >= k) t = cand;
+  }
+  // every pick against every other (k broadcasts)
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) rank[s] = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < EPL; ++s2) {
+    uint64_t m = __ballot(key[s2] >= t);
+    while (m) {
+      const int src = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const uint64_t kj = readlane64(key[s2], src);
+#pragma unroll
+      for (int s = 0; s < EPL; ++s) rank[s] += (kj > key[s]) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < EPL; ++s)
+    if (key[s] < t) rank[s] = k;
+}
+
 // Top-k of one token: ids/weights to global memory (and ids to LDS).
 template <int EPL>
 __device__ void topk_token(const float* __restrict__ row, int E, int k, int lane,
@@ -64,7 +123,10 @@ __device__ void topk_token(const float* __restrict__ row, int E, int k, int lane
                            int32_t* lds_ids) {
   float val[EPL];
   int rank[EPL];
-  rank_token<EPL>(row, E, lane, val, rank);
+  if constexpr (EPL == 1)
+    rank_token<EPL>(row, E, lane, val, rank);
+  else
+    rank_picks<EPL>(row, E, k, lane, val, rank);
   // the best logit (rank 0) for a stable softmax
   float vbest = 0.0f;
 #pragma unroll
