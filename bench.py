@@ -156,9 +156,9 @@ def build_layers(wl, L, dev, first_layer=0):
 
 
 def fused_route(wl):
-    """A single token with at most 64 experts: the route/sort is folded into
+    """A single token with at most 128 experts: the route/sort is folded into
     the gate_up launch (gnf4_route_gemm_one_token), unless --unfused-route."""
-    return wl.T == 1 and wl.E <= 64 and not UNFUSED_ROUTE
+    return wl.T == 1 and wl.E <= 128 and not UNFUSED_ROUTE
 
 
 def gate_up(wl, ly):

@@ -427,8 +427,9 @@ gnf4_status gnf4_route_gemm_one_token(const float* logits, int64_t E, int32_t to
                                       void* workspace, size_t workspace_bytes, void* stream) {
   if (E < 1 || top_k < 1 || top_k > E || N <= 0 || K < kBlock || K % kBlock != 0)
     return GNF4_ERR_INVALID_ARG;
-  // one expert per lane of the ranking wavefront; top_k as gnf4_route_sort
-  if (E > 64 || top_k > 32) return GNF4_ERR_UNSUPPORTED;
+  // at most two experts per lane of the ranking wavefronts; top_k as
+  // gnf4_route_sort
+  if (E > 128 || top_k > 32) return GNF4_ERR_UNSUPPORTED;
   if (N * (K / 2) >= ((int64_t)1 << 31) || E * N >= ((int64_t)1 << 31)) return GNF4_ERR_UNSUPPORTED;
   if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
   const void* out4[] = {topk_ids, topk_w, expert_offsets, sorted_slots, group_sizes,

@@ -293,7 +293,9 @@ __device__ __forceinline__ void dword_terms(uint32_t d, const float (&xw)[R][8],
 // table when the gather is fused), (2) the first row chunk's activations,
 // (3) every weight chunk of the lane, step by step; the decode then consumes
 // the weights in the same order.
-template <int L, int NU, int R, int STEPS, typename AbsT, bool ROUTED = false>
+// ROUTED = 0: groups from sizes/ids; 1 or 2: a single token routed in the
+// launch, over up to 64 * ROUTED experts (ROUTED router entries per lane).
+template <int L, int NU, int R, int STEPS, typename AbsT, int ROUTED = 0>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
@@ -307,40 +309,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // and the group this workgroup serves
   int my_slot = 0;
   GroupRef gr;
-  if constexpr (ROUTED) {
-    // One token routed in the launch.  Lane e holds expert e's key, as the
-    // route/sort kernels build it (rank_token); its rank, the number of
-    // larger keys, is counted by the wavefronts together, each against
-    // 64 / kWaves of the keys, and summed through LDS: the same integers
-    // rank_token gives.  Group j is the j-th pick in expert order, one row
-    // (row j, token 0).
+  if constexpr (ROUTED > 0) {
+    // One token routed in the launch.  Entry s of lane l holds expert
+    // l + 64 s's key, as the route/sort kernels build it (rank_token); its
+    // rank, the number of larger keys, is counted by the wavefronts together,
+    // each against the keys of 64 / kWaves of the lanes, and summed through
+    // LDS: the same integers rank_token gives.  Group j is the j-th pick in
+    // expert order, one row (row j, token 0).
+    constexpr int EPL = ROUTED;
     constexpr int kKeys = kWave / kWaves;
     static_assert(kKeys * kWaves == kWave, "the keys split evenly over the wavefronts");
-    __shared__ int s_part[kWaves][kWave];
+    __shared__ int s_part[kWaves][EPL][kWave];
     const int E = a.ro.E;
-    float val[1];
-    int rank[1];
-    val[0] = lane < E ? a.route_logits[lane] : 0.0f;
-    const uint64_t key = lane < E ? (((uint64_t)float_key(val[0]) << 32) |
-                                     (uint32_t)(0xffffffffu - (uint32_t)lane))
-                                  : 0ull;
-    int part = 0;
+    float val[EPL];
+    int rank[EPL];
+    uint64_t key[EPL];
 #pragma unroll
-    for (int q = 0; q < kKeys; ++q) part += readlane64(key, kKeys * wave + q) > key ? 1 : 0;
-    s_part[wave][lane] = part;
+    for (int s = 0; s < EPL; ++s) {
+      const int e = lane + kWave * s;
+      val[s] = e < E ? a.route_logits[e] : 0.0f;
+      key[s] = e < E ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
+                     : 0ull;
+    }
+    int part[EPL];
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) part[s] = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < EPL; ++s2)
+#pragma unroll
+      for (int q = 0; q < kKeys; ++q) {
+        const uint64_t kj = readlane64(key[s2], kKeys * wave + q);
+#pragma unroll
+        for (int s = 0; s < EPL; ++s) part[s] += kj > key[s] ? 1 : 0;
+      }
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) s_part[wave][s][lane] = part[s];
     __syncthreads();
-    rank[0] = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) rank[0] += s_part[w][lane];
+    for (int s = 0; s < EPL; ++s) {
+      rank[s] = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) rank[s] += s_part[w][s][lane];
+    }
+    // the j-th pick in expert order (entry 0 of every lane, then entry 1)
     const int j = blockIdx.y;
-    uint64_t m = __ballot(rank[0] < a.ro.K);
-    for (int q = 0; q < j; ++q) m &= m - 1;  // uniform: j < K picks
+    int jj = j;
+    gr.expert = 0;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) {
+      uint64_t m = __ballot(rank[s] < a.ro.K);
+      const int c = __popcll(m);
+      if (jj >= 0 && jj < c) {  // uniform
+        for (int q = 0; q < jj; ++q) m &= m - 1;
+        gr.expert = kWave * s + __ffsll((unsigned long long)m) - 1;
+      }
+      jj -= c;
+    }
     gr.g = j;
     gr.size = 1;
-    gr.expert = __ffsll((unsigned long long)m) - 1;
     gr.row = j;
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0)
-      route_one_token_write<1>(a.ro, lane, val, rank);
+      route_one_token_write<EPL>(a.ro, lane, val, rank);
   } else {
     if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
     if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y,
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     for (int r = 0; r < R; ++r) {
       const int row = r0 + r;
       xrow[r] = row < r_end ? row : -1;
-      if constexpr (ROUTED) {
+      if constexpr (ROUTED > 0) {
         xrow[r] = row < r_end ? 0 : -1;  // every pick reads the one token
         continue;
       }
@@ -516,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeKArgs a) 
   }
 }
 
-template <int L, int NU, int R, int STEPS, typename AbsT, bool ROUTED = false>
+template <int L, int NU, int R, int STEPS, typename AbsT, int ROUTED = 0>
 hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   // one staging round must cover the split's activation rows
   if (p.L != L || p.steps != STEPS || p.R != R || p.cps > L * STEPS ||
@@ -529,18 +558,30 @@ hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t str
   return hipGetLastError();
 }
 
-// The routed launch: one activation row per group (R = 1).
-template <int L, typename AbsT>
+// The routed launch: one activation row per group (R = 1); EPL router
+// entries per lane (E <= 64 * EPL).
+template <int L, typename AbsT, int EPL>
 hipError_t launch_L_routed(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
   if (p.R != 1) return hipErrorInvalidValue;
   switch (p.steps * 16 + p.NU) {
-    case 16 + 4: return launch_one<L, 4, 1, 1, AbsT, true>(a, p, stream);
-    case 16 + 2: return launch_one<L, 2, 1, 1, AbsT, true>(a, p, stream);
-    case 16 + 1: return launch_one<L, 1, 1, 1, AbsT, true>(a, p, stream);
-    case 32 + 2: return launch_one<L, 2, 1, 2, AbsT, true>(a, p, stream);
-    case 32 + 1: return launch_one<L, 1, 1, 2, AbsT, true>(a, p, stream);
-    case 48 + 1: return launch_one<L, 1, 1, 3, AbsT, true>(a, p, stream);
-    case 64 + 1: return launch_one<L, 1, 1, 4, AbsT, true>(a, p, stream);
+    case 16 + 4: return launch_one<L, 4, 1, 1, AbsT, EPL>(a, p, stream);
+    case 16 + 2: return launch_one<L, 2, 1, 1, AbsT, EPL>(a, p, stream);
+    case 16 + 1: return launch_one<L, 1, 1, 1, AbsT, EPL>(a, p, stream);
+    case 32 + 2: return launch_one<L, 2, 1, 2, AbsT, EPL>(a, p, stream);
+    case 32 + 1: return launch_one<L, 1, 1, 2, AbsT, EPL>(a, p, stream);
+    case 48 + 1: return launch_one<L, 1, 1, 3, AbsT, EPL>(a, p, stream);
+    case 64 + 1: return launch_one<L, 1, 1, 4, AbsT, EPL>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename AbsT, int EPL>
+hipError_t launch_routed_L(const DecodeKArgs& a, const DecodePlan& p, hipStream_t stream) {
+  switch (p.L) {
+    case 64: return launch_L_routed<64, AbsT, EPL>(a, p, stream);
+    case 32: return launch_L_routed<32, AbsT, EPL>(a, p, stream);
+    case 16: return launch_L_routed<16, AbsT, EPL>(a, p, stream);
+    case 8: return launch_L_routed<8, AbsT, EPL>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -697,24 +738,13 @@ hipError_t launch_decode_routed(const GemmArgs& g, const DecodePlan& p, const fl
   DecodeKArgs a = decode_args(g, p);
   a.route_logits = logits;
   a.ro = ro;
+  if (ro.E > 2 * kWave) return hipErrorInvalidValue;
+  const bool two = ro.E > kWave;
   hipError_t err;
-  if (g.abs_bf16) {
-    switch (p.L) {
-      case 64: err = launch_L_routed<64, uint16_t>(a, p, stream); break;
-      case 32: err = launch_L_routed<32, uint16_t>(a, p, stream); break;
-      case 16: err = launch_L_routed<16, uint16_t>(a, p, stream); break;
-      case 8: err = launch_L_routed<8, uint16_t>(a, p, stream); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (p.L) {
-      case 64: err = launch_L_routed<64, float>(a, p, stream); break;
-      case 32: err = launch_L_routed<32, float>(a, p, stream); break;
-      case 16: err = launch_L_routed<16, float>(a, p, stream); break;
-      case 8: err = launch_L_routed<8, float>(a, p, stream); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (g.abs_bf16)
+    err = two ? launch_routed_L<uint16_t, 2>(a, p, stream) : launch_routed_L<uint16_t, 1>(a, p, stream);
+  else
+    err = two ? launch_routed_L<float, 2>(a, p, stream) : launch_routed_L<float, 1>(a, p, stream);
   // the split-K reduce runs after the launch: the groups and slots it reads
   // are the route/sort outputs the launch wrote
   if (err != hipSuccess || p.S == 1) return err;

@@ -215,7 +215,7 @@ def route_sort(logits, top_k, buffers=None):
 def route_gemm_one_token(logits, x, packed, absmax, top_k, buffers=None, y=None,
                          workspace=None):
     """A batch-1 decode step's route/sort and grouped GEMM in one launch:
-    ``logits`` [1, E] fp32 (E <= 64), ``x`` [1, K] bf16, the packed stack as
+    ``logits`` [1, E] fp32 (E <= 128), ``x`` [1, K] bf16, the packed stack as
     grouped_gemm takes it.  Returns (y [top_k, N] in grouped order, the
     RouteResult written into ``buffers``, as route_sort gives for T = 1)."""
     _need(logits, "logits", torch.float32, 2)

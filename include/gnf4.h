@@ -175,8 +175,9 @@ gnf4_status gnf4_route_sort(const float* logits, int64_t T, int64_t E, int32_t t
  *                     bytes for split-K partials (16-byte aligned); with
  *                     less the call runs unsplit
  *
- * Limits: 1 <= E <= 64 (GNF4_ERR_UNSUPPORTED above: one expert per lane of
- * the ranking wavefront), 1 <= top_k <= min(E, 32) as gnf4_route_sort,
+ * Limits: 1 <= E <= 128 (GNF4_ERR_UNSUPPORTED above: at most two experts per
+ * lane of the ranking wavefronts), 1 <= top_k <= min(E, 32) as
+ * gnf4_route_sort,
  * K % 64 == 0, N * K/2 < 2^31.
  * Tolerance and determinism as gnf4_grouped_gemm.  Errors:
  * GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_UNSUPPORTED,

@@ -3,8 +3,9 @@ route/sort folded into the grouped GEMM's launch): every route/sort output
 equals the oracle's, and gnf4_route_sort's, bit for bit (weights: the same
 bits as gnf4_route_sort, within 1e-6 of the oracle); y meets the GEMM bound
 against the oracle on the routed rows.  Cases: OLMoE's shape, few experts,
-ragged K, tied logits, bf16 absmax, and a K that forces split-K (whose reduce
-reads the groups the launch wrote).  Experts that are not picked hold 0xFF
+ragged K, tied logits, bf16 absmax, a K that forces split-K (whose reduce
+reads the groups the launch wrote), and 65 to 128 experts (two router entries
+per lane: Qwen3's and GPT-OSS's expert counts, ties across the two entries).  Experts that are not picked hold 0xFF
 codes and NaN absmax, so reading a wrong expert shows up as NaN.
 """
 
@@ -70,7 +71,9 @@ def _check(c, what, runs=2):
 
 
 @pytest.mark.parametrize("E,k,N,K", [(64, 8, 2048, 2048), (8, 2, 384, 512), (60, 4, 256, 2880),
-                                     (1, 1, 64, 64), (64, 32, 128, 256)])
+                                     (1, 1, 64, 64), (64, 32, 128, 256), (65, 8, 256, 512),
+                                     (128, 8, 1536, 2048), (128, 4, 384, 2880),
+                                     (100, 32, 128, 256)])
 def test_route_gemm_shapes(E, k, N, K):
     _check(_case(E, k, N, K, seed=E * 131 + k), f"E={E} k={k} N={N} K={K}")
 
@@ -88,6 +91,21 @@ def test_route_gemm_tied_logits():
     lg[0, [5, 6, 60]] = -0.0
     lg[0, 33] = 1.5
     _check(_case(64, 6, 192, 512, seed=7, logits=lg), "tied logits")
+
+
+@pytest.mark.parametrize("name", ["qwen3_t1", "gptoss"])
+def test_route_gemm_128_expert_workloads(name):
+    wl = wls.WORKLOADS[name]
+    K, N = wl.gemm("gate_up")
+    _check(_case(wl.E, wl.top_k, N, K, seed=6, logits=wls.router_logits(wl)), f"{name} gate_up")
+
+
+def test_route_gemm_tied_logits_two_entries():
+    lg = np.zeros((1, 128), np.float32)
+    lg[0, [3, 67, 100, 36]] = 2.0        # ties between a lane's two entries
+    lg[0, [64, 0]] = -0.0
+    lg[0, 127] = 2.0
+    _check(_case(128, 6, 192, 512, seed=8, logits=lg), "tied logits, 128 experts")
 
 
 def test_route_gemm_bf16_absmax():

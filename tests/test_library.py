@@ -90,7 +90,7 @@ def test_route_gemm_one_token_rejects_bad_arguments(lib):
     args = [None, 64, 8, None, None, None, 0, 256, 512, None, None, None, None, None, None, None,
             None, None, None, 0, None]
     bad_e = list(args)
-    bad_e[1] = 65                       # more experts than lanes of the ranking wavefront
+    bad_e[1] = 129                      # more than two experts per lane of the ranking wavefronts
     assert f(*bad_e) == 3               # GNF4_ERR_UNSUPPORTED
     bad_k = list(args)
     bad_k[2] = 65                       # top_k above E
