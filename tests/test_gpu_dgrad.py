@@ -118,6 +118,16 @@ def test_dgrad_team_widths(K, sizes, ids, M):
     check_gemm(dx, c["o"], c["written"], f"dgrad K={K} sizes={sizes}")
 
 
+def test_dgrad_many_splits():
+    """Three one-row groups of K = 2048 over N = 1536 weight rows: the launch
+    rule splits N 24 ways, so the reduce sums two batches of split partials,
+    the second one padded."""
+    note("dgrad 24 N splits")
+    c = _custom(4, 1536, 2048, [1, 1, 1], [0, 2, 3], 3, seed=24)
+    dx = _run(c, workspace=None, path=DEC)
+    check_gemm(dx, c["o"], c["written"], "dgrad 24 splits")
+
+
 def _absmax_scenarios(E, N, K):
     """Weight magnitudes that stress the tile path's per-column-block scale:
     blocks alternating 1e-30 / 1e30 along K, one row 1e4 above the others,
