@@ -158,6 +158,28 @@ def test_glue_argument_errors(lib):
     assert lib.gnf4_combine(FAKE, FAKE, FAKE, 1 << 29, 8, 8, 64, FAKE, NULL) == 3  # T*k >= 2^31
 
 
+def test_route_workspace_follows_the_chunk_rule(lib):
+    """Up to 32 tokens sort in one launch with no workspace; beyond that,
+    chunks of 16 tokens keep one int32 count per (chunk, expert)."""
+    q = lib.gnf4_route_sort_workspace_size
+    assert q(1, 64, 8) == 0
+    assert q(32, 128, 8) == 0
+    assert q(33, 128, 8) == 3 * 128 * 4
+    assert q(4096, 256, 8) == 256 * 256 * 4
+
+
+def test_dgrad_split_rule(lib):
+    """The decode-path dgrad's N split, seen through its workspace size (fp32
+    partials [S, M, K]) on a 256-CU device (the size a host without a device
+    plans for): about two wavefronts per SIMD, each split at least one batch
+    of 8 rows per team; rows of 32 chunks use 32-lane teams, two per
+    wavefront, so OLMoE down splits 16 ways where 64-lane teams split 32."""
+    q = lib.gnf4_grouped_dgrad_workspace_size
+    assert q(8, 2048, 2048, 8, 64) == 32 * 8 * 2048 * 4    # OLMoE gate_up: 64-lane teams
+    assert q(8, 2048, 1024, 8, 64) == 16 * 8 * 1024 * 4    # OLMoE down: 32-lane teams
+    assert q(3, 1536, 2048, 3, 4) == 24 * 3 * 2048 * 4     # three rows, 24 splits
+
+
 def test_no_cpu_fallback_in_binding():
     """The binding never routes through the oracle or a torch fallback."""
     src = open(os.path.join(ROOT, "grouped_nf4_expert_amd", "gnf4.py")).read()
