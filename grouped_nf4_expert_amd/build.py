@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgnf4.so")
 SOURCES = ["api.hip", "pack.hip", "route.hip", "gather.hip", "decode.hip", "tile.hip",
-           "glue.hip", "dgrad.hip"]
+           "glue.hip", "dgrad.hip", "validate.hip"]
 ARCH = "gfx950"
 
 

@@ -49,10 +49,17 @@ bool is_device_ptr(const void* p) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Workspace of one grouped GEMM call: the tile path's activation-row
-// exponents (M int32) first, then the decode path's split-K partials, each
-// region 256-byte aligned.
-size_t row_exp_bytes(int64_t M) { return ((size_t)M * sizeof(int32_t) + 255) & ~(size_t)255; }
+// Workspace of one grouped GEMM call: the tile path's staged activation
+// rows first (stage_bytes: the exponents of M + 1 rows, then M + 1 fp16 rows
+// of the padded width; fewer are used when the rows are staged per token),
+// then the decode path's split-K partials, each region 256-byte aligned.
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+void set_stage_regions(void* ws, int64_t M, int32_t*& row_exp, uint16_t*& xh) {
+  row_exp = static_cast<int32_t*>(ws);
+  xh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                   align256((size_t)(M + 1) * sizeof(int32_t)));
+}
 
 }  // namespace
 
@@ -209,6 +216,8 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
   a.y = y;
   a.partial = nullptr;
   a.row_exp = nullptr;
+  a.xh = nullptr;
+  a.xh_ld = 0;
   a.E = (int)E;
   a.N = (int)N;
   a.K = (int)K;
@@ -234,15 +243,25 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
     if (M <= kDecodeMaxRows) run_tile = false;
   }
   const hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    int32_t bad = 0;
+    const hipError_t ve = validate_groups(sizes, ids, G, E, M, slots, T * (int64_t)slot_div, s,
+                                          &bad);
+    if (ve != hipSuccess) return hip_fail(ve);
+    if (bad) return GNF4_ERR_INVALID_ARG;
+  }
   size_t dec_off = 0;  // where the decode partials start in the workspace
   if (ws && (run_tile || ws_bytes > 0)) {
     if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
     if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
   }
+  StagePlan sp{};
   if (run_tile) {
-    dec_off = row_exp_bytes(M);
+    dec_off = stage_bytes(M, K);
     if (!ws || ws_bytes < dec_off) return GNF4_ERR_WORKSPACE;
-    a.row_exp = static_cast<int32_t*>(ws);
+    set_stage_regions(ws, M, a.row_exp, a.xh);
+    sp = plan_stage(a);
+    a.xh_ld = sp.ld;
   }
   if (run_decode) {
     DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
@@ -261,7 +280,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
     if (e != hipSuccess) return hip_fail(e);
   }
   if (run_tile) {
-    hipError_t e = launch_row_exp(a, s);
+    hipError_t e = launch_stage_x(a, sp, a.mxfp4, s);  // MXFP4 operands in natural K order
     if (e == hipSuccess) e = launch_tile(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -299,7 +318,7 @@ size_t gnf4_grouped_dgrad_workspace_size_ex(int64_t M, int64_t N, int64_t K, int
                                             int64_t E, int32_t path) {
   (void)E;
   if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
-  if (dgrad_path(path, M, G, N % 8 == 0) == 2) return row_exp_bytes(M);
+  if (dgrad_path(path, M, G, N % 8 == 0) == 2) return stage_bytes(M, N);
   return dgrad_workspace_bytes(plan_dgrad(M, N, K, G, device_cu_count()), M, K);
 }
 
@@ -345,14 +364,21 @@ gnf4_status gnf4_grouped_dgrad_ex(const uint16_t* dy, const uint8_t* packed, con
   a.G = (int)G;
   a.M = (int)M;
   const hipStream_t s = (hipStream_t)stream;
+  if (validate_requested()) {
+    int32_t bad = 0;
+    const hipError_t ve = validate_groups(group_sizes, group_expert_ids, G, E, M, nullptr, 0, s,
+                                          &bad);
+    if (ve != hipSuccess) return hip_fail(ve);
+    if (bad) return GNF4_ERR_INVALID_ARG;
+  }
   const bool tile_ok = dgrad_tile_ok(dy, N);
   const int run = dgrad_path(path, M, G, tile_ok);
   if (run == 2) {
     if (!tile_ok) return GNF4_ERR_UNSUPPORTED;  // forced tile path, dy not in 16-byte chunks
-    if (!workspace || workspace_bytes < row_exp_bytes(M)) return GNF4_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < stage_bytes(M, N)) return GNF4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GNF4_ERR_INVALID_ARG;
     if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;
-    // per-row exponents of dy, by the forward's pre-pass over an [M, N] matrix
+    // dy staged by the forward's pre-pass as an [M, N] matrix, natural order
     GemmArgs g{};
     g.x = dy;
     g.slots = nullptr;
@@ -360,9 +386,10 @@ gnf4_status gnf4_grouped_dgrad_ex(const uint16_t* dy, const uint8_t* packed, con
     g.T = 0;
     g.M = (int)M;
     g.K = (int)N;
-    g.row_exp = static_cast<int32_t*>(workspace);
-    hipError_t e = launch_row_exp(g, s);
-    if (e == hipSuccess) e = launch_dgrad_tile(a, g.row_exp, 1, s);
+    set_stage_regions(workspace, M, g.row_exp, g.xh);
+    const StagePlan sp = plan_stage(g);
+    hipError_t e = launch_stage_x(g, sp, true, s);
+    if (e == hipSuccess) e = launch_dgrad_tile(a, g.row_exp, g.xh, sp.ld, 1, s);
     return e == hipSuccess ? GNF4_OK : hip_fail(e);
   }
   DgradPlan p = plan_dgrad(M, N, K, G, device_cu_count());
@@ -544,7 +571,7 @@ size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int6
   if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
   const bool tile_only = path == 2 || (path == 0 && auto_tile_only(M, G));
   const bool tile = tile_only || (path == 0 && M > kDecodeMaxRows);
-  const size_t tile_bytes = tile ? row_exp_bytes(M) : 0;
+  const size_t tile_bytes = tile ? stage_bytes(M, K) : 0;
   if (tile_only) return tile_bytes;
   const DecodePlan p = plan_decode(M, N, K, G, split_k, device_cu_count());
   return tile_bytes + decode_workspace_bytes(p, M, N);

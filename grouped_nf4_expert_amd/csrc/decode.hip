@@ -36,7 +36,6 @@
 //    order (deterministic).
 
 #include <limits.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -694,19 +693,7 @@ static DecodePlan plan_decode_rule(int64_t M, int64_t N, int64_t K, int64_t G, i
 }
 
 DecodePlan plan_decode(int64_t M, int64_t N, int64_t K, int64_t G, int split_k, int num_cus) {
-  DecodePlan p = plan_decode_rule(M, N, K, G, split_k, num_cus);
-#ifdef GNF4_TUNING  // experiment builds only: override the rows per lane
-  if (const char* v = getenv("GNF4_TUNE_NU")) {
-    const int nu = atoi(v);
-    if (p.L != 0 && (nu == 1 || nu == 2 || nu == 4) && nu * p.steps <= kMaxLoads &&
-        nu * p.R <= kMaxLoads) {
-      p.NU = nu;
-      p.rows_per_block = kWaves * (kWave / p.L) * p.NU;
-      p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
-    }
-  }
-#endif
-  return p;
+  return plan_decode_rule(M, N, K, G, split_k, num_cus);
 }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N) {

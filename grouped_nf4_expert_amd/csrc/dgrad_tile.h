@@ -7,10 +7,10 @@
 namespace gnf4 {
 
 // dx = dy . dequant(W[expert]) for every group of at least `rows_min` rows.
-// `row_exp` holds one power-of-two exponent per dy row, as launch_row_exp
-// writes them for an [M, N] matrix.  Requires N % 8 == 0 and 16-byte
-// aligned dy (rows are read in 16-byte chunks).
-hipError_t launch_dgrad_tile(const DgradArgs& a, const int32_t* row_exp, int rows_min,
-                             hipStream_t stream);
+// dy is read as launch_stage_x staged it for an [M, N] matrix (natural
+// order): `dyh` [M + 1, ld] fp16 rows, row M all zeros, and `row_exp`
+// [M + 1] their power-of-two exponents.
+hipError_t launch_dgrad_tile(const DgradArgs& a, const int32_t* row_exp, const uint16_t* dyh,
+                             int ld, int rows_min, hipStream_t stream);
 
 }  // namespace gnf4

@@ -173,9 +173,13 @@ __device__ __forceinline__ bool find_group(const int32_t* sizes, const int32_t* 
   return false;
 }
 
-// Upper bound on the groups with at least `lo` rows among G groups of M rows.
+// Upper bound on the groups with at least `lo` rows that start inside M
+// rows, among G groups: the first c - 1 of c such groups end before the
+// last one starts, so (c - 1) lo <= M - 1, i.e. c <= ceil(M / lo).  (The
+// last group may be clipped at M: sizes [9, 9] with M = 17 are two groups.)
 inline int64_t group_slots(int64_t G, int64_t M, int64_t lo) {
-  const int64_t cap = M / (lo > 0 ? lo : 1);
+  const int64_t l = lo > 0 ? lo : 1;
+  const int64_t cap = (M + l - 1) / l;
   return G < cap ? G : cap;
 }
 
@@ -210,7 +214,12 @@ struct GemmArgs {
   const int32_t* ids;
   uint16_t* y;
   float* partial;     // split-K partials [S, M, N] (decode path)
-  int32_t* row_exp;   // per-row power-of-two exponent of the activations [M] (tile path)
+  // Tile path: the activation rows staged once by stage_x as fp16 times a
+  // power of two per row (xh [rows + 1, xh_ld], row `rows` all zeros) and
+  // the exponents (row_exp [rows + 1]); see launch_stage_x.
+  int32_t* row_exp;
+  uint16_t* xh;
+  int xh_ld;
   // Optional fused gather: when `slots` is set, output row r uses activation
   // row slots[r] / slot_div of x (x is then [T, K]); a slot outside
   // [0, T * slot_div) leaves row r unwritten.
@@ -236,7 +245,26 @@ size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N);
 
 hipError_t launch_decode(const GemmArgs& a, const DecodePlan& p, hipStream_t stream);
 hipError_t launch_tile(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_row_exp(const GemmArgs& a, hipStream_t stream);
+
+// Activation staging for the matrix-core kernels.  Rows are those of x
+// itself (one per token row when the gather is fused and T <= M, else one
+// per output row r < M, read through its slot), each written once as fp16
+// times 2^t (t chosen per row so its largest |x| lands in [2^14, 2^15);
+// every bf16 value within 2^28 of the row's largest converts exactly) into
+// xh [rows + 1, ld] with ld = kStageAlign-padded K, zero-filled past K and
+// in the MFMA operand order of the weight format (NF4: each 8 elements as
+// {0, 2, 4, 6, 1, 3, 5, 7}; MXFP4 and the dgrad: natural order); row
+// `rows` is all zeros (the source of absent rows) and row_exp[rows] = 0.
+constexpr int kStageAlign = 128;
+struct StagePlan {
+  int rows;        // staged rows (T or M), plus one zero row
+  bool by_token;   // rows are token rows of x (fused gather)
+  int ld;          // fp16 elements per staged row
+};
+StagePlan plan_stage(const GemmArgs& g);
+size_t stage_bytes(int64_t rows, int64_t width);  // row_exp + xh for `rows` rows, 256-aligned
+hipError_t launch_stage_x(const GemmArgs& g, const StagePlan& p, bool natural_order,
+                          hipStream_t stream);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* slots, int top_k, int T, int M, int K,
                          uint16_t* out, hipStream_t stream);
@@ -271,5 +299,16 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* slot_rows, const flo
                           hipStream_t stream);
 
 int device_cu_count();
+
+// Opt-in check of device-resident grouping inputs (validate.hip).
+// validate_requested(): GNF4_VALIDATE=1 in the environment (read per call).
+// validate_groups() runs the check on `stream`, waits for it and stores in
+// `result` a nonzero bit set when a size is negative, a non-empty group's id
+// lies outside [0, E), the sizes sum past M, or (slots given) a covered row's
+// slot lies outside [0, slot_lim).
+bool validate_requested();
+hipError_t validate_groups(const int32_t* sizes, const int32_t* ids, int64_t G, int64_t E,
+                           int64_t M, const int32_t* slots, int64_t slot_lim,
+                           hipStream_t stream, int32_t* result);
 
 }  // namespace gnf4

@@ -11,13 +11,16 @@
 // an element-wise tolerance of 8e-3 |y| + 1e-3 rms(y) at K in the thousands,
 // while fp16 weights rounded ONCE from the fp32 product absmax * level are
 // well inside it.  So each weight row n gets a power-of-two scale 2^-s_n that
-// brings its largest block absmax into [0.5, 1); codes are decoded straight
-// to fp16(level * absmax * 2^-s_n) (fp32 product, one rounding).  Each
-// activation row m gets its own power-of-two scale 2^t_m (a pre-pass over the
-// rows, row_exp_kernel) that puts its largest |x| in [2^14, 2^15), so every
-// bf16 value converts to fp16 exactly whatever the row's magnitude (down to
-// 2^-28 of the row maximum, below which values no longer matter), with no
-// overflow.  Products accumulate in fp32 on the matrix core and the epilogue
+// brings its largest block absmax into [2^14, 2^15); codes are decoded
+// straight to fp16(level * absmax * 2^-s_n) (fp32 product, one rounding).
+// Every block whose absmax lies within 2^25 of its row's largest then
+// decodes to normal fp16 numbers (the smallest nonzero level is 0.0796), so
+// its values carry fp16's full 11 bits however far below the row's largest
+// it sits; only blocks further down lose bits in fp16's subnormals.  Each
+// activation row m is staged once (stage_x_kernel) as fp16 times its own
+// power of two 2^t_m that puts its largest |x| in [2^14, 2^15): every bf16
+// value within 2^28 of the row's largest converts exactly.  Products (at
+// most 2^30) accumulate in fp32 on the matrix core and the epilogue
 // multiplies by 2^(s_n - t_m) exactly before rounding to bf16.
 //
 // Work layout (XCD-aware): a workgroup of 8 wavefronts owns one (group, 256
@@ -33,10 +36,12 @@
 //    straight from HBM into registers, builds the 16-entry fp16 table of that
 //    block (16 products, 8 packs, 8 byte-plane permutes) and decodes 8 codes
 //    per dword with v_perm_b32 byte lookups -- no LDS traffic for weights;
-//  * activations: the group's rows x 128 K of bf16 are staged through LDS as
-//    fp16 (double-buffered, rows padded to 272 bytes so the 16-byte fragment
-//    reads are bank-conflict-free) and stored in the same K order the weight
-//    decode produces, so A and B fragments agree slot by slot.
+//  * activations: the group's rows x 128 K of the staged fp16 rows, already
+//    in the K order the weight decode produces (so A and B fragments agree
+//    slot by slot), are copied through LDS (double-buffered, rows padded to
+//    272 bytes so the 16-byte fragment reads are bank-conflict-free); the
+//    copy has no conversion and no bounds tests: staged rows are padded to a
+//    multiple of 128 and absent rows read the staged zero row.
 
 #include <limits.h>
 
@@ -50,6 +55,10 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector: copies of it stay in registers (a HIP uint4
+// struct copied into LDS can become a memcpy that keeps its source in
+// scratch memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;      // 8 wavefronts, two per SIMD
 constexpr int kTileN = 256;        // output columns per workgroup (32 per wavefront)
@@ -61,7 +70,7 @@ constexpr int kLdsRow = kStepK + 8;  // fp16 elements per staged row (padded)
 
 struct TileKArgs {
   GemmArgs g;
-  bool exp_by_token;  // row_exp holds one exponent per token row of x (fused gather)
+  StagePlan st;  // the staged activation rows (xh, row_exp) and their indexing
   int n_tiles;
   int n_work;   // group slots * n_tiles
 };
@@ -121,39 +130,6 @@ __device__ __forceinline__ half8 decode8(uint32_t d, const Table& t) {
   return r;
 }
 
-// 8 bf16 (natural K order), times 2^t when SCALED, -> 8 fp16 in the
-// decode's slot order (NATURAL: K order, for MXFP4 whose convert yields the
-// low-nibble element first).  The row's exponent keeps every value below
-// 2^15, and bf16 values in the fp16 normal range convert exactly, so
-// round-toward-zero packing is exact.
-template <bool SCALED, bool NATURAL = false>
-__device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v, int t) {
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[2 * j] = __uint_as_float(d[j] << 16);
-    f[2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
-    if constexpr (SCALED) {
-      f[2 * j] = ldexpf(f[2 * j], t);
-      f[2 * j + 1] = ldexpf(f[2 * j + 1], t);
-    }
-  }
-  uint4 r;
-  if constexpr (NATURAL) {
-    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
-    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3]));
-    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[5]));
-    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[6], f[7]));
-  } else {
-    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[2]));
-    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[4], f[6]));
-    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[1], f[3]));
-    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[5], f[7]));
-  }
-  return r;
-}
-
 // The stack's scale type names its format: fp32 or bf16 block absmax (NF4),
 // or uint8 E8M0 scales (MXFP4: E2M1 codes, one scale per 32, low nibble
 // first).
@@ -179,7 +155,8 @@ __device__ __forceinline__ half8 mx_decode8(uint32_t d, float scale) {
 struct PassCtx {
   const TileKArgs* a;
   _Float16* s_x;           // [2][kPassRows * kLdsRow]
-  int* s_exp;              // [kPassRows] activation exponents of the pass's rows
+  const int* s_src;        // [kPassRows] staged row of each of the pass's rows
+  const int* s_exp;        // [kPassRows] their activation exponents
   const uint8_t* wrow;     // this lane's weight row (or row 0 when out of range)
   const void* arow;        // its absmax row (fp32, or bf16 bits)
   bool n_ok;               // the lane's column exists
@@ -200,11 +177,10 @@ __device__ __forceinline__ int div_slot(int n, int d) {
 // is a compile-time constant so the row-tile loops carry no branches: every
 // MFMA of a sub-step and its A-fragment reads are issued back to back, and
 // the next sub-step's decode can overlap them.  Loads are unconditional (an
-// absent row or column reads an always-valid address) and what is absent is
-// dropped where the values are used: zero activations at staging, a zero
-// decode table for an absent weight block.
+// absent row reads the staged zero row, an absent column an always-valid
+// weight address) and an absent weight block decodes through a zero table.
 template <int RT, typename AbsT>
-__device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
+__device__ __forceinline__ void tile_pass(const PassCtx& c) {
   const GemmArgs& g = c.a->g;
   constexpr int kChunks = RT;  // 16-byte x chunks per thread: RT*32 rows x 16 chunks / 512 threads
   float16v acc[RT];
@@ -214,54 +190,36 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
     for (int v = 0; v < 16; ++v) acc[rt][v] = 0.0f;
 
   const int total_steps = c.n_steps + (c.rem_k ? 1 : 0);
-  // source row of each staged chunk (-1: absent, staged as zeros)
-  int xsrc[kChunks];
+  // staged source of each chunk this thread copies (row-major staged rows,
+  // 16 chunks of 8 fp16 per row and step)
+  const uint16_t* xsrc[kChunks];
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
-    const int row = (c.tid + kThreads * j) >> 4;
-    int src = -1;
-    if (row < c.rows) {
-      src = c.p0 + row;
-      if (g.slots) {
-        const int slot = g.slots[c.p0 + row];
-        src = (slot >= 0 && slot < g.T * g.slot_div) ? div_slot(slot, g.slot_div) : -1;
-      }
-    }
-    xsrc[j] = src;
+    const int q = c.tid + kThreads * j;
+    xsrc[j] = g.xh + (size_t)c.s_src[q >> 4] * g.xh_ld + 8 * (q & 15);
   }
-  // the pass's activation scale exponents, in LDS for staging and epilogue
 
   // Two register sets (activations and weights) alternate between steps so
   // every load is issued two steps before it is used: step s computes from
   // LDS buffer s % 2, then stages step s + 1's activations (loaded during
   // step s - 1) into the other buffer; one barrier per step.  The step loop
   // is unrolled by two so the register sets are static.
-  uint4 xr[2][kChunks];
+  u32x4 xr[2][kChunks];
   uint4 wc[2][2];
   float wa[2];
   auto load_x = [&](auto slot_c, int step) {
     constexpr int sl = decltype(slot_c)::value;
-    const int k0 = step * kStepK;
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int c16 = (c.tid + kThreads * j) & 15;
-      const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
-      xr[sl][j] = *reinterpret_cast<const uint4*>(
-          g.x + (ok ? (size_t)xsrc[j] * c.K + k0 + 8 * c16 : 0));
-    }
+    for (int j = 0; j < kChunks; ++j)
+      xr[sl][j] = *reinterpret_cast<const u32x4*>(xsrc[j] + step * kStepK);
   };
-  auto store_x = [&](auto slot_c, int buf, int step) {
+  auto store_x = [&](auto slot_c, int buf) {
     constexpr int sl = decltype(slot_c)::value;
-    const int k0 = step * kStepK;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
       const int q = c.tid + kThreads * j;
-      const int row = q >> 4, c16 = q & 15;
-      const bool ok = xsrc[j] >= 0 && k0 + 8 * c16 < c.K;
-      const uint4 v = ok ? xr[sl][j] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&c.s_x[buf * (kPassRows * kLdsRow) + row * kLdsRow + 8 * c16]) =
-          scaled ? bf16x8_to_f16_slots<true, kTileMx<AbsT>>(v, c.s_exp[row])
-                 : bf16x8_to_f16_slots<false, kTileMx<AbsT>>(v, 0);
+      *reinterpret_cast<u32x4*>(
+          &c.s_x[buf * (kPassRows * kLdsRow) + (q >> 4) * kLdsRow + 8 * (q & 15)]) = xr[sl][j];
     }
   };
   // weight codes: the lane's 32 bytes of block h of the step, and its absmax
@@ -321,7 +279,7 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[rt], bw, acc[rt], 0, 0, 0);
     }
     if (step < last) {
-      store_x(SO{}, 1 - sl, step + 1);
+      store_x(SO{}, 1 - sl);
       __syncthreads();
     }
   };
@@ -330,7 +288,7 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
   load_w(S0{}, 0);
   load_x(S1{}, min(1, last));
   load_w(S1{}, min(1, last));
-  store_x(S0{}, 0, 0);
+  store_x(S0{}, 0);
   __syncthreads();
   for (int step = 0; step < total_steps; step += 2) {
     do_step(S0{}, step);
@@ -370,6 +328,7 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c, bool scaled) {
 template <typename AbsT>
 __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][kPassRows * kLdsRow];
+  __shared__ int s_src[kPassRows];
   __shared__ int s_exp[kPassRows];
 
   // XCD-aware order: consecutive work items land on one XCD.
@@ -398,16 +357,17 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   const int spr = kTileMx<AbsT> ? 2 * bpr : bpr;  // scales per weight row
   const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) + (size_t)e * N * spr;
 
-  // activation exponent of output row `row` (by token when the gather is
-  // fused and the exponents were taken per token); the first pass's are
-  // loaded now, so their latency overlaps the absmax loads below
-  auto row_exp_of = [&](int row) -> int {
-    if (!a.exp_by_token) return a.g.row_exp[row];
+  // staged row of output row `row`: its token's row when the rows were
+  // staged per token (fused gather; an invalid slot reads the zero row),
+  // else the row itself
+  auto staged_row = [&](int row) -> int {
+    if (!a.st.by_token) return row;
     const int slot = a.g.slots[row];
-    return (slot >= 0 && slot < a.g.T * a.g.slot_div) ? a.g.row_exp[div_slot(slot, a.g.slot_div)]
-                                                       : 0;
+    return (slot >= 0 && slot < a.g.T * a.g.slot_div) ? div_slot(slot, a.g.slot_div) : a.st.rows;
   };
-  const int t_first = tid < min(kPassRows, r_end - r_begin) ? row_exp_of(r_begin + tid) : 0;
+  // the first pass's staged rows are looked up now, so their latency
+  // overlaps the absmax loads below
+  const int src_first = tid < min(kPassRows, r_end - r_begin) ? staged_row(r_begin + tid) : a.st.rows;
 
   // per-row power-of-two scale from the row's largest block absmax
   const int n = n_wave + i;
@@ -456,12 +416,15 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
       if (!n_ok) m = 0.0f;
     }
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    // m = f * 2^sexp with f in [0.5, 1): m * 2^-(sexp - 15) lies in [2^14, 2^15)
     (void)frexpf(m, &sexp);
+    sexp -= 15;
   }
 
   PassCtx c;
   c.a = &a;
   c.s_x = &s_x[0][0];
+  c.s_src = s_src;
   c.s_exp = s_exp;
   c.wrow = wexp + (n_ok ? (size_t)n * row_bytes : 0);
   c.arow = aexp + (n_ok ? (size_t)n * spr : 0);
@@ -481,21 +444,21 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
   for (int p0 = r_begin; p0 < r_end; p0 += kPassRows) {
     c.p0 = p0;
     c.rows = min(kPassRows, r_end - p0);
-    // the pass's activation exponents (prefetched for the first pass); rows
-    // of ordinary magnitude have exponent 0, and a pass scales only when one
-    // of its rows needs it
-    int t = 0;
-    if (tid < c.rows) {
-      t = p0 == r_begin ? t_first : row_exp_of(p0 + tid);
-      s_exp[tid] = t;
+    // the pass's staged rows (looked up ahead for the first pass) and their
+    // exponents; rows past the group read the zero row
+    if (tid < kPassRows) {
+      int src = a.st.rows;
+      if (tid < c.rows) src = p0 == r_begin ? src_first : staged_row(p0 + tid);
+      s_src[tid] = src;
+      s_exp[tid] = a.g.row_exp[src];
     }
-    const bool scaled = __syncthreads_or(t) != 0;
+    __syncthreads();
     switch ((c.rows + 31) / 32) {
-      case 1: tile_pass<1, AbsT>(c, scaled); break;
-      case 2: tile_pass<2, AbsT>(c, scaled); break;
-      case 3: tile_pass<3, AbsT>(c, scaled); break;
-      case 4: tile_pass<4, AbsT>(c, scaled); break;
-      default: tile_pass<5, AbsT>(c, scaled); break;
+      case 1: tile_pass<1, AbsT>(c); break;
+      case 2: tile_pass<2, AbsT>(c); break;
+      case 3: tile_pass<3, AbsT>(c); break;
+      case 4: tile_pass<4, AbsT>(c); break;
+      default: tile_pass<5, AbsT>(c); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
@@ -514,16 +477,16 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(TileKArgs a) {
 //    64-code absmax block) at row n0 + l, columns k0 + 32 w, and decodes them
 //    through the fp16 table of fp16(level * absmax * 2^-S), one rounding,
 //    where 2^-S puts the largest block absmax of that 64-column block over
-//    all N rows into [0.5, 1) (the contraction mixes rows, so the scale is
-//    per output column, applied exactly in the epilogue);
-//  * dy: the pass's rows x 64 n staged as fp16 times each row's 2^t_r, as
-//    the forward stages activations (t_r from the row-exponent pre-pass over
-//    dy);
+//    all N rows into [2^14, 2^15) (the contraction mixes rows, so the scale
+//    is per output column, applied exactly in the epilogue);
+//  * dy: the rows as stage_x_kernel staged them (fp16 times each row's 2^t_r,
+//    natural order, rows padded to a multiple of 128 with zeros; absent rows
+//    read the zero row);
 //  * fp32 accumulation on v_mfma_f32_32x32x16_f16, dx = acc * 2^(S - t_r)
 //    rounded once to bf16.
-// A block whose absmax lies 2^24 or more below its column block's largest
-// flushes toward zero in fp16, the range limit of the forward tile path
-// with the roles of rows and columns exchanged.
+// Every block whose absmax lies within 2^25 of its column block's largest
+// decodes to normal fp16 numbers, the forward tile path's range with the
+// roles of rows and columns exchanged.
 constexpr int kDgThreads = 512;    // 8 wavefronts (two per SIMD), 32 output columns each
 constexpr int kDgTileK = 256;      // output columns (of K) per workgroup
 constexpr int kDgBlocks = kDgTileK / kBlock;  // absmax blocks a tile's columns span
@@ -531,10 +494,13 @@ constexpr int kDgStepN = 64;       // rows of W (contraction) per step
 constexpr int kDgRowTiles = 5;     // 32-row MFMA tiles per pass
 constexpr int kDgPassRows = 32 * kDgRowTiles;
 constexpr int kDgLds = kDgStepN + 8;  // fp16 per LDS row: 144 bytes, conflict-free reads
+static_assert(kStageAlign % kDgStepN == 0, "staged dy rows cover every step of N");
 
 struct DgradTileKArgs {
   DgradArgs d;
-  const int32_t* row_exp;
+  const int32_t* row_exp;  // [M + 1] exponents of the staged dy rows
+  const uint16_t* dyh;     // [M + 1, ld] staged dy rows, row M all zeros
+  int ld;
   int rows_min;
   int k_tiles;
   int n_work;  // group slots * k_tiles
@@ -552,8 +518,8 @@ struct DgPassCtx {
 };
 
 template <int RT, typename AbsT>
-__device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
-  const DgradArgs& d = c.a->d;
+__device__ __forceinline__ void dgrad_pass(const DgPassCtx& c) {
+  const DgradTileKArgs& a = *c.a;
   float16v acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -566,9 +532,17 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
   const bool k_ok = kk < c.K;
   // 16-byte dy chunks per thread: RT * 32 rows x 8 chunks over the threads
   constexpr int kChunks = (RT * 256 + kDgThreads - 1) / kDgThreads;
+  const uint16_t* ysrc[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int q = c.tid + kDgThreads * j;
+    const int row = q >> 3;
+    const int src = (q < RT * 256 && row < c.rows) ? c.p0 + row : a.d.M;
+    ysrc[j] = a.dyh + (size_t)src * a.ld + 8 * (q & 7);
+  }
   uint4 wr;
   float war;
-  uint4 yr[kChunks];
+  u32x4 yr[kChunks];
   // Loads of step s are issued at the top of step s - 1 and consumed (staged
   // into LDS) at its end, so no loaded register lives across the loop's
   // back edge.
@@ -579,12 +553,8 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
     war = absmax_at(static_cast<const AbsT*>(c.aexp) + (ok ? (size_t)n * c.bpr : 0),
                     ok ? kk / kBlock : 0);
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int q = c.tid + kDgThreads * j;
-      const int row = q >> 3, nn = step * kDgStepN + 8 * (q & 7);
-      const bool okr = q < RT * 256 && row < c.rows && nn < c.N;
-      yr[j] = *reinterpret_cast<const uint4*>(d.dy + (okr ? (size_t)(c.p0 + row) * c.N + nn : 0));
-    }
+    for (int j = 0; j < kChunks; ++j)
+      yr[j] = *reinterpret_cast<const u32x4*>(ysrc[j] + step * kDgStepN);
   };
   auto stage = [&](int buf, int step) {
     const int n = step * kDgStepN + c.lane;
@@ -607,13 +577,8 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
     for (int j = 0; j < kChunks; ++j) {
       const int q = c.tid + kDgThreads * j;
       if (kChunks * kDgThreads > RT * 256 && q >= RT * 256) break;
-      const int row = q >> 3, c8 = q & 7;
-      const int nn = step * kDgStepN + 8 * c8;
-      const bool okr = row < c.rows && nn < c.N;
-      const uint4 v = okr ? yr[j] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&c.s_dy[buf * (kDgPassRows * kDgLds) + row * kDgLds + 8 * c8]) =
-          scaled ? bf16x8_to_f16_slots<true, true>(v, c.s_exp[row])
-                 : bf16x8_to_f16_slots<false, true>(v, 0);
+      *reinterpret_cast<u32x4*>(
+          &c.s_dy[buf * (kDgPassRows * kDgLds) + (q >> 3) * kDgLds + 8 * (q & 7)]) = yr[j];
     }
   };
 
@@ -650,7 +615,7 @@ __device__ __forceinline__ void dgrad_pass(const DgPassCtx& c, bool scaled) {
     for (int v = 0; v < 16; ++v) {
       const int row = rt * 32 + 8 * (v >> 2) + 4 * c.h + (v & 3);
       if (row >= c.rows) continue;
-      d.dx[(size_t)(c.p0 + row) * c.K + k] =
+      a.d.dx[(size_t)(c.p0 + row) * c.K + k] =
           f32_to_bf16(ldexpf(acc[rt][v], c.sexp - c.s_exp[row]));
     }
 }
@@ -715,8 +680,10 @@ __global__ __launch_bounds__(kDgThreads, 1) void dgrad_tile_kernel(DgradTileKArg
   float m = 0.0f;
 #pragma unroll
   for (int w = 0; w < kDgThreads / kWave; ++w) m = fmaxf(m, s_max[wave >> 1][w]);
+  // m = f * 2^sexp with f in [0.5, 1): m * 2^-(sexp - 15) lies in [2^14, 2^15)
   int sexp = 0;
   (void)frexpf(m, &sexp);
+  sexp -= 15;
 
   DgPassCtx c;
   c.a = &a;
@@ -738,47 +705,63 @@ __global__ __launch_bounds__(kDgThreads, 1) void dgrad_tile_kernel(DgradTileKArg
   for (int p0 = r_begin; p0 < r_end; p0 += kDgPassRows) {
     c.p0 = p0;
     c.rows = min(kDgPassRows, r_end - p0);
-    int t = 0;
-    if (tid < c.rows) t = a.row_exp[p0 + tid];
-    if (tid < kDgPassRows) s_exp[tid] = t;
-    const bool scaled = __syncthreads_or(t) != 0;
+    if (tid < kDgPassRows) s_exp[tid] = tid < c.rows ? a.row_exp[p0 + tid] : 0;
+    __syncthreads();
     switch ((c.rows + 31) / 32) {
-      case 1: dgrad_pass<1, AbsT>(c, scaled); break;
-      case 2: dgrad_pass<2, AbsT>(c, scaled); break;
-      case 3: dgrad_pass<3, AbsT>(c, scaled); break;
-      case 4: dgrad_pass<4, AbsT>(c, scaled); break;
-      default: dgrad_pass<5, AbsT>(c, scaled); break;
+      case 1: dgrad_pass<1, AbsT>(c); break;
+      case 2: dgrad_pass<2, AbsT>(c); break;
+      case 3: dgrad_pass<3, AbsT>(c); break;
+      case 4: dgrad_pass<4, AbsT>(c); break;
+      default: dgrad_pass<5, AbsT>(c); break;
     }
     __syncthreads();  // the next pass reuses the LDS buffers
   }
 }
 
-// Activation scale exponents, one wavefront per row: per token row of x
-// when `by_token` (fused gather), else per output row r < M with its source
-// (x row r, or its token through the fused gather's slot).  From the
-// largest |x| from the bf16 bit patterns (magnitude order is integer order)
-// and e, the biased exponent of that maximum.  A row whose maximum lies in
-// [2^-6, 2^15) converts to fp16 as it is (t = 0: values down to 2^-14 are
-// exact and smaller ones carry at most 2^-24 absolute error, far inside the
-// tolerance next to such a row's size); any other row gets t = 141 - e, so
-// that max * 2^t lies in [2^14, 2^15).  A row of zeros (or a skipped slot)
-// gets t = 0.
-constexpr int kExpThreads = 256;
+// Activation staging for the matrix-core kernels, one wavefront per staged
+// row.  The row's source is x's own row (token rows, or rows without a
+// gather), or for an output row read through the fused gather its token's
+// row (an invalid slot, like the extra last row, stages zeros).  From the
+// largest |x| -- taken on the bf16 bit patterns, whose magnitude order is
+// integer order -- and e, its biased exponent, t = 141 - e puts that
+// largest value times 2^t in [2^14, 2^15) (a row of zeros gets t = 0).
+// Every value is then written as fp16(x * 2^t): x * 2^t is exact in fp32,
+// and exact in fp16 down to 2^-14, i.e. for every value within 2^28 of the
+// row's largest; smaller ones round to fp16's subnormals (nearest, ties to
+// even).  Elements past the row's end up to the padded width are zeros.
+constexpr int kStageThreads = 256;
 
-__global__ __launch_bounds__(kExpThreads) void row_exp_kernel(GemmArgs g, bool by_token) {
+struct StageKArgs {
+  const uint16_t* x;
+  const int32_t* slots;  // read per output row when the rows are not token rows
+  int slot_div, T;
+  int rows;              // staged rows; row `rows` is the zero row
+  bool gather_rows;      // rows are output rows read through `slots`
+  int K, ld;
+  bool natural;          // natural K order (else the NF4 decode's slot order)
+  uint16_t* xh;
+  int32_t* row_exp;
+};
+
+__device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__global__ __launch_bounds__(kStageThreads) void stage_x_kernel(StageKArgs s) {
   const int lane = threadIdx.x % kWave;
-  const int waves = gridDim.x * (kExpThreads / kWave);
-  const int chunks = g.K / 8;
-  const int n_rows = by_token ? g.T : g.M;
-  for (int r = blockIdx.x * (kExpThreads / kWave) + threadIdx.x / kWave; r < n_rows; r += waves) {
-    int src = r;
-    if (g.slots && !by_token) {
-      const int slot = g.slots[r];
-      src = (slot >= 0 && slot < g.T * g.slot_div) ? slot / g.slot_div : -1;
+  const int waves = gridDim.x * (kStageThreads / kWave);
+  const int chunks = s.K / 8;
+  for (int r = blockIdx.x * (kStageThreads / kWave) + threadIdx.x / kWave; r <= s.rows;
+       r += waves) {
+    int src = r < s.rows ? r : -1;
+    if (s.gather_rows && src >= 0) {
+      const int slot = s.slots[r];
+      src = (slot >= 0 && slot < s.T * s.slot_div) ? slot / s.slot_div : -1;
     }
+    const uint4* row = reinterpret_cast<const uint4*>(s.x + (size_t)(src >= 0 ? src : 0) * s.K);
     uint32_t mb = 0;
     if (src >= 0) {
-      const uint4* row = reinterpret_cast<const uint4*>(g.x + (size_t)src * g.K);
       for (int c0 = lane; c0 < chunks; c0 += 4 * kWave) {
         uint4 v[4];
 #pragma unroll
@@ -796,33 +779,79 @@ __global__ __launch_bounds__(kExpThreads) void row_exp_kernel(GemmArgs g, bool b
       }
     }
     mb = wave_max_u32(mb);
-    const int e = (int)(mb >> 7);
-    if (lane == 0) g.row_exp[r] = (mb == 0 || (e >= 121 && e <= 141)) ? 0 : 141 - e;
+    const int t = mb == 0 ? 0 : 141 - (int)(mb >> 7);
+    uint4* out = reinterpret_cast<uint4*>(s.xh + (size_t)r * s.ld);
+    for (int c = lane; c < s.ld / 8; c += kWave) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (src >= 0 && c < chunks) v = row[c];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = ldexpf(__uint_as_float(d[j] << 16), t);
+        f[2 * j + 1] = ldexpf(__uint_as_float(d[j] & 0xffff0000u), t);
+      }
+      uint4 o;
+      if (s.natural) {
+        o = make_uint4(f16x2_rne(f[0], f[1]), f16x2_rne(f[2], f[3]), f16x2_rne(f[4], f[5]),
+                       f16x2_rne(f[6], f[7]));
+      } else {
+        // the NF4 decode's slot order: elements {0, 2, 4, 6, 1, 3, 5, 7}
+        o = make_uint4(f16x2_rne(f[0], f[2]), f16x2_rne(f[4], f[6]), f16x2_rne(f[1], f[3]),
+                       f16x2_rne(f[5], f[7]));
+      }
+      out[c] = o;
+    }
+    if (lane == 0) s.row_exp[r] = t;
   }
 }
 
 }  // namespace
 
-// With the gather fused, token rows repeat top_k times among the M rows: the
-// exponents are then taken once per token (T <= M entries fit the buffer).
-static bool exp_by_token(const GemmArgs& g) { return g.slots != nullptr && g.T <= g.M; }
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-hipError_t launch_row_exp(const GemmArgs& g, hipStream_t stream) {
-  const bool by_token = exp_by_token(g);
-  const int n_rows = by_token ? g.T : g.M;
-  if (n_rows <= 0) return hipSuccess;
-  const int per_block = kExpThreads / kWave;
+size_t stage_bytes(int64_t rows, int64_t width) {
+  const int64_t ld = (width + kStageAlign - 1) / kStageAlign * kStageAlign;
+  return align256((size_t)(rows + 1) * sizeof(int32_t)) +
+         align256((size_t)(rows + 1) * (size_t)ld * sizeof(uint16_t));
+}
+
+// With the gather fused, token rows repeat top_k times among the M rows: they
+// are staged once per token (T <= M entries fit the workspace sized for M).
+StagePlan plan_stage(const GemmArgs& g) {
+  StagePlan p;
+  p.by_token = g.slots != nullptr && g.T <= g.M;
+  p.rows = p.by_token ? g.T : g.M;
+  p.ld = (g.K + kStageAlign - 1) / kStageAlign * kStageAlign;
+  return p;
+}
+
+hipError_t launch_stage_x(const GemmArgs& g, const StagePlan& p, bool natural_order,
+                          hipStream_t stream) {
+  StageKArgs s;
+  s.x = g.x;
+  s.slots = g.slots;
+  s.slot_div = g.slot_div;
+  s.T = g.T;
+  s.rows = p.rows;
+  s.gather_rows = g.slots != nullptr && !p.by_token;
+  s.K = g.K;
+  s.ld = p.ld;
+  s.natural = natural_order;
+  s.xh = g.xh;
+  s.row_exp = g.row_exp;
+  const int per_block = kStageThreads / kWave;
   const int cap = device_cu_count() * 8;
-  int blocks = (n_rows + per_block - 1) / per_block;
+  int blocks = (p.rows + 1 + per_block - 1) / per_block;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(row_exp_kernel, dim3(blocks), dim3(kExpThreads), 0, stream, g, by_token);
+  hipLaunchKernelGGL(stage_x_kernel, dim3(blocks), dim3(kStageThreads), 0, stream, s);
   return hipGetLastError();
 }
 
 hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   TileKArgs a;
   a.g = g;
-  a.exp_by_token = exp_by_token(g);
+  a.st = plan_stage(g);
   a.n_tiles = (g.N + kTileN - 1) / kTileN;
   a.n_work = (int)group_slots(g.G, g.M, g.rows_min_tile) * a.n_tiles;
   const int grid = ((a.n_work + 7) / 8) * 8;
@@ -836,11 +865,13 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_dgrad_tile(const DgradArgs& d, const int32_t* row_exp, int rows_min,
-                             hipStream_t stream) {
+hipError_t launch_dgrad_tile(const DgradArgs& d, const int32_t* row_exp, const uint16_t* dyh,
+                             int ld, int rows_min, hipStream_t stream) {
   DgradTileKArgs a;
   a.d = d;
   a.row_exp = row_exp;
+  a.dyh = dyh;
+  a.ld = ld;
   a.rows_min = rows_min;
   a.k_tiles = (d.K + kDgTileK - 1) / kDgTileK;
   a.n_work = (int)group_slots(d.G, d.M, rows_min) * a.k_tiles;

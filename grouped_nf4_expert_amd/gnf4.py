@@ -417,3 +417,4 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
             _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
             path, split_k, adt, _stream()), "gnf4_grouped_gemm_gather")
     return y
+

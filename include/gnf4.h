@@ -34,6 +34,14 @@
  *    live on the device (group sizes, expert ids) are not read by the host:
  *    kernels skip a group whose size is <= 0 or whose expert id is outside
  *    [0, E), and never touch rows at or beyond M.
+ *  - Opt-in validation: with GNF4_VALIDATE=1 in the environment (read at
+ *    every call), each grouped GEMM and dgrad call first runs a check kernel
+ *    on `stream`, waits for it (the call then synchronises the host with the
+ *    stream, so this mode is for debugging, not for graph capture) and
+ *    returns GNF4_ERR_INVALID_ARG without launching anything when a group
+ *    size is negative, a non-empty group's expert id lies outside [0, E),
+ *    the sizes sum past M, or (fused gather) a covered row's slot lies
+ *    outside [0, T * top_k): everything a kernel would otherwise skip.
  */
 #ifndef GNF4_H_
 #define GNF4_H_
@@ -267,20 +275,25 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
  *   workspace         device scratch of gnf4_grouped_dgrad_workspace_size()
  *                     bytes (16-byte aligned): the GEMV path's split-N fp32
  *                     partials (with less, that path runs unsplit: correct,
- *                     slower), or the tile path's per-row exponents of dy
- *                     (4 M bytes rounded up to 256; required)
+ *                     slower), or the tile path's staged dy rows (required:
+ *                     4 (M + 1) bytes of exponents and an fp16 copy of
+ *                     2 (M + 1) ceil128(N) bytes, each rounded up to 256)
  *
  * Two kernels meet one contract, |dx - exact| <= 8e-3 |exact| + 1e-3
  * rms(exact) per element, deterministic run to run:
  *  - GEMV path: fp32 decode and accumulation, splits of N summed in fixed
  *    order.  Every weight byte is read once per pass of up to 4 rows of dy,
  *    so it suits groups of few rows (decode-sized batches).
- *  - tile path (matrix cores): codes decoded once per 128 rows of a group
- *    into fp16 scaled by a power of two per 64-column block of K (its largest
- *    absmax over the N rows), dy rows staged in fp16 with a power of two per
- *    row, fp16 x fp16 -> fp32 MFMA, the scales applied exactly at the end.
- *    Needs N % 8 == 0 and a 16-byte aligned dy.  A block whose absmax lies
- *    2^24 or more below its column block's largest flushes toward zero.
+ *  - tile path (matrix cores): codes decoded once per 160 rows of a group
+ *    into fp16 scaled by a power of two per 64-column block of K (putting
+ *    its largest absmax over the N rows in [2^14, 2^15)), dy rows staged
+ *    once in fp16 with a power of two per row (putting the row's largest in
+ *    [2^14, 2^15)), fp16 x fp16 -> fp32 MFMA, the scales applied exactly at
+ *    the end.  Needs N % 8 == 0 and a 16-byte aligned dy.  Range: a block
+ *    whose absmax lies within 2^25 of its column block's largest, and a dy
+ *    value within 2^28 of its row's largest, enter the product with fp16's
+ *    full precision; values further down round to fp16 subnormals (and
+ *    below 2^-24 of the staged scale, to zero).
  * gnf4_grouped_dgrad chooses automatically: the tile path for a batch
  * averaging at least 32 rows per group (M >= 32 min(G, M)) when dy allows
  * it, else the GEMV path.
@@ -378,21 +391,30 @@ gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const floa
  *   y                 [M, N] bf16 bits out; only rows covered by a valid group
  *                     are written, the rest keep their contents
  *   workspace         device scratch of gnf4_grouped_gemm_workspace_size() bytes,
- *                     16-byte aligned: the tile path's per-row activation
- *                     exponents (4 M bytes, rounded up to 256) and, when the
- *                     decode path splits K, its fp32 partials
+ *                     16-byte aligned: the tile path's staged activation rows
+ *                     (4 (M + 1) bytes of per-row exponents and an fp16 copy
+ *                     of 2 (M + 1) ceil128(K) bytes, each rounded up to 256;
+ *                     with the fused gather only T + 1 rows are used) and,
+ *                     when the decode path splits K, its fp32 partials
  *
  * Group g covers rows [sum_{g'<g} max(size_g', 0), + size_g) clipped to M.
  * Routing weights are not applied here (the top-k combine is separate glue).
  * Two kernels implement the same arithmetic contract: a bandwidth-bound
  * decode path for groups with few rows (fp32 decode and multiply-add, optional
  * split-K with a fixed-order fp32 reduce) and a matrix-core tile path for
- * groups with many rows (a power-of-two scale per weight row and per
- * activation row, codes decoded with their block absmax into fp16, fp16 x
- * fp16 -> fp32 MFMA).  Which one runs is a performance choice made from
- * host-known sizes only; both meet |y - exact| <= 8e-3 |exact| +
- * 1e-3 rms(exact) per element for any finite bf16 activations.  Results are
- * deterministic run to run.  The automatic choice: groups of up to 8 rows
+ * groups with many rows (a power-of-two scale per weight row putting its
+ * largest block absmax in [2^14, 2^15), codes decoded with their block
+ * absmax into fp16; each activation row staged once as fp16 times a power of
+ * two putting its largest |x| in [2^14, 2^15); fp16 x fp16 -> fp32 MFMA).
+ * Which one runs is a performance choice made from host-known sizes only;
+ * both meet |y - exact| <= 8e-3 |exact| + 1e-3 rms(exact) per element.  The
+ * decode path does so for any finite inputs.  The tile path's range: every
+ * block whose absmax lies within 2^25 of its weight row's largest, and every
+ * activation within 2^28 of its row's largest, enters the product with
+ * fp16's full precision whatever the row's magnitude; smaller ones round to
+ * fp16 subnormals (below 2^-24 of the staged scale, to zero), which matters
+ * only when such values carry an output.  Results are deterministic run to
+ * run.  The automatic choice: groups of up to 8 rows
  * take the decode path and larger ones the tile path, except that a batch
  * averaging at least 32 rows per group (M >= 32 min(G, M), prefill) runs
  * every group on the tile path and launches no decode kernel.

@@ -243,3 +243,23 @@ def test_dgrad_bf16_absmax(name, gemm, path):
     o, written = oracle.ref_grouped_dgrad(host_f64(dy), p_ref, a_ref, ref["group_sizes"],
                                           ref["group_expert_ids"])
     check_gemm(dx, o, written, f"dgrad bf16 absmax {name}/{gemm}")
+
+
+@pytest.mark.parametrize("gap", [8, 16, 24])
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_dgrad_block_range(gap, path):
+    """Weight rows 2^gap below the largest in every column block carry the
+    whole gradient: dy is zero against the large (even) rows.  The tile path
+    scales each 64-column block of K so its largest absmax over the N rows
+    lands in [2^14, 2^15), so blocks within 2^25 of it decode exactly."""
+    E, N, K, M = 2, 128, 512, 40
+    w_scale = np.ones((E, N, K), np.float32)
+    w_scale[:, 1::2, :] = 2.0 ** -gap
+    dy_scale = np.ones((M, N), np.float32)
+    dy_scale[:, 0::2] = 0.0
+    c = _custom(E, N, K, [24, 16], [1, 0], M, seed=90 + gap, w_scale=w_scale, dy_scale=dy_scale)
+    note(f"dgrad block range 2^-{gap} path={path}")
+    dx = gnf4.grouped_dgrad(c["dy"], c["packed"], c["absmax"], c["sizes"], c["ids"], path=path)
+    torch.cuda.synchronize()
+    check_gemm(dx, c["o"], c["written"], f"dgrad block gap 2^{gap} path {path}")
+

@@ -130,6 +130,10 @@ BOUNDARY_CASES = {
     # a prefill-sized batch (at least 32 rows per group on average) holding
     # groups of 1, 2 and 8 rows: the automatic path runs all on the tile path
     "prefill_small_groups": (5, 96, 256, [1, 8, 150, 2, 60], [4, 0, 3, 1, 2], 221),
+    # two tile-sized groups (9 rows each, just past the decode path's 8) in 17
+    # rows: the second is clipped at M, and the tile launch must still give
+    # it a slot (ceil(M / 9) = 2 groups, not floor = 1)
+    "tile_groups_clipped_at_M": (2, 64, 128, [9, 9], [0, 1], 17),
 }
 
 
@@ -205,6 +209,51 @@ def test_adversarial_absmax(scenario, path):
     note(f"gemm adversarial absmax {scenario} path={path}")
     y = _run_custom(c, path)
     check_gemm(y, c["y_ref"], c["written"], f"{scenario} path {path}")
+
+
+@pytest.mark.parametrize("gap", [8, 14, 16, 20, 24])
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_weight_block_range(gap, path):
+    """Blocks whose absmax lies 2^gap below their weight row's largest carry
+    the whole output: the activations are zero against the large (even)
+    blocks.  The tile path scales each weight row so its largest block absmax
+    lands in [2^14, 2^15), so every block within 2^25 of it decodes to normal
+    fp16 numbers; every gap here is inside that range on both paths."""
+    E, N, K, M = 2, 96, 1024, 40
+    scale = np.ones((E, N, K), np.float32)
+    for b in range(1, K // 64, 2):
+        scale[:, :, 64 * b:64 * (b + 1)] = 2.0 ** -gap
+    rng = np.random.default_rng(70 + gap)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    for b in range(0, K // 64, 2):
+        x[:, 64 * b:64 * (b + 1)] = 0.0
+    c = _custom(E, N, K, [24, 16], [1, 0], M, seed=70 + gap, w_scale=scale,
+                x=wls.bf16_round(x))
+    note(f"gemm weight block range 2^-{gap} path={path}")
+    y = _run_custom(c, path)
+    check_gemm(y, c["y_ref"], c["written"], f"block gap 2^{gap} path {path}")
+
+
+@pytest.mark.parametrize("gap", [10, 12, 20, 27])
+@pytest.mark.parametrize("row_max", [2.0 ** -5, 1.0, 2.0 ** 20])
+@pytest.mark.parametrize("path", [DEC, TILE])
+def test_activation_entries_below_row_max(gap, row_max, path):
+    """Each activation row holds its largest value at k = 0, where every
+    weight is zero, and the rest of the row 2^gap smaller: the small entries
+    carry every output.  The tile path stages each row as fp16 scaled so its
+    largest lands in [2^14, 2^15), so entries within 2^28 of it are exact,
+    whatever the row's own magnitude."""
+    E, N, K, M = 2, 96, 512, 40
+    scale = np.ones((E, N, K), np.float32)
+    scale[:, :, 0] = 0.0
+    rng = np.random.default_rng(80 + gap)
+    x = rng.standard_normal((M, K)) * (row_max * 2.0 ** -gap)
+    x[:, 0] = row_max
+    c = _custom(E, N, K, [24, 16], [0, 1], M, seed=80 + gap, w_scale=scale,
+                x=wls.bf16_round(x.astype(np.float32)))
+    note(f"gemm activation entries 2^-{gap} below a row max {row_max:g} path={path}")
+    y = _run_custom(c, path)
+    check_gemm(y, c["y_ref"], c["written"], f"x gap 2^{gap}, max {row_max:g}, path {path}")
 
 
 @pytest.mark.parametrize("name,gemm", [("olmoe", "gate_up"), ("gptoss", "down"),

@@ -186,3 +186,4 @@ def test_no_cpu_fallback_in_binding():
     assert "oracle" not in src
     for line in src.splitlines():
         assert "import numpy" not in line
+
