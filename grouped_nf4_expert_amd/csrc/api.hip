@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dgrad_tile.h"
 #include "gnf4_internal.h"
 #include "route_core.h"
@@ -59,6 +61,36 @@ void set_stage_regions(void* ws, int64_t M, int32_t*& row_exp, uint16_t*& xh) {
   row_exp = static_cast<int32_t*>(ws);
   xh = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
                                    align256((size_t)(M + 1) * sizeof(int32_t)));
+}
+
+// Workspace of gnf4_grouped_gemm_gather_noalloc: one library-owned array per
+// GPU, held until the process ends.  Its host-side name is only a stand-in;
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device (scratch_address).
+constexpr size_t kNoAllocScratchBytes = (size_t)GNF4_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -180,7 +212,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
                                const int32_t* ids, int64_t G, int64_t M, uint16_t* y,
                                void* ws, size_t ws_bytes, int32_t path, int32_t split_k,
                                void* stream, const int32_t* slots = nullptr, int32_t slot_div = 1,
-                               int64_t T = 0) {
+                               int64_t T = 0, bool ws_is_scratch = false) {
   if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0)
     return GNF4_ERR_INVALID_ARG;
   if (path < 0 || path > 2 || split_k < 0 || split_k > 16) return GNF4_ERR_INVALID_ARG;
@@ -253,7 +285,7 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
   size_t dec_off = 0;  // where the decode partials start in the workspace
   if (ws && (run_tile || ws_bytes > 0)) {
     if (!aligned(ws, 16)) return GNF4_ERR_INVALID_ARG;
-    if (!is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
+    if (!ws_is_scratch && !is_device_ptr(ws)) return GNF4_ERR_NOT_DEVICE_PTR;
   }
   StagePlan sp{};
   if (run_tile) {
@@ -563,6 +595,33 @@ gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t
   return gemm_common(x, packed, absmax, absmax_dtype, E, N, K, group_sizes, group_expert_ids, G,
                      M, y, workspace, workspace_bytes, path, split_k, stream, sorted_slots, top_k,
                      T);
+}
+
+size_t gnf4_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+gnf4_status gnf4_grouped_gemm_gather_noalloc(const uint16_t* x, int64_t T,
+                                             const int32_t* sorted_slots, int32_t top_k,
+                                             const uint8_t* packed, const void* absmax, int64_t E,
+                                             int64_t N, int64_t K, const int32_t* group_sizes,
+                                             const int32_t* group_expert_ids, int64_t G,
+                                             int64_t M, uint16_t* y, int32_t path,
+                                             int32_t split_k, int32_t absmax_dtype,
+                                             void* stream) {
+  if (!sorted_slots) return GNF4_ERR_INVALID_ARG;
+  if (E <= 0 || N <= 0 || K < kBlock || K % kBlock != 0 || M < 0 || G < 0 || T < 0 ||
+      top_k < 1)
+    return GNF4_ERR_INVALID_ARG;
+  if (path < 0 || path > 2 || split_k < 0 || split_k > 16) return GNF4_ERR_INVALID_ARG;
+  if (M == 0 || G == 0) return GNF4_OK;
+  // the scratch must hold what the workspace of gnf4_grouped_gemm_gather would
+  const size_t need = gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, path, split_k);
+  if (need > kNoAllocScratchBytes) return GNF4_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  return gemm_common(x, packed, absmax, absmax_dtype, E, N, K, group_sizes, group_expert_ids, G,
+                     M, y, ws, kNoAllocScratchBytes, path, split_k, stream, sorted_slots, top_k,
+                     T, true);
 }
 
 size_t gnf4_grouped_gemm_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,

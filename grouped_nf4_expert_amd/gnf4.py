@@ -98,6 +98,11 @@ def library():
     lib.gnf4_grouped_gemm_ex.restype = ctypes.c_int
     lib.gnf4_grouped_gemm_ex.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp,
                                          sz, i32, i32, i32, vp]
+    lib.gnf4_noalloc_scratch_bytes.restype = sz
+    lib.gnf4_noalloc_scratch_bytes.argtypes = []
+    lib.gnf4_grouped_gemm_gather_noalloc.restype = ctypes.c_int
+    lib.gnf4_grouped_gemm_gather_noalloc.argtypes = [vp, i64, vp, i32, vp, vp, i64, i64, i64, vp,
+                                                     vp, i64, i64, vp, i32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -416,5 +421,33 @@ def grouped_gemm(x_sorted, packed, absmax, group_sizes, group_expert_ids, G=None
             _ptr(x_sorted), rows, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(absmax), E, N, K,
             _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), _ptr(workspace), ws_bytes,
             path, split_k, adt, _stream()), "gnf4_grouped_gemm_gather")
+    return y
+
+
+def grouped_gemm_gather_noalloc(x, sorted_slots, top_k, packed, absmax, group_sizes,
+                                group_expert_ids, y, G=None, path=PATH_AUTO, split_k=0):
+    """gnf4_grouped_gemm_gather_noalloc: the fused-gather grouped GEMM with
+    its workspace in the library's static per-GPU scratch array, writing
+    into the caller's ``y`` [M, N] (nothing is allocated, here or in the
+    library).  Raises Gnf4Error (GNF4_ERR_UNSUPPORTED) when the call needs
+    more workspace than gnf4_noalloc_scratch_bytes()."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(sorted_slots, "sorted_slots", torch.int32, 1)
+    _need(packed, "packed", torch.uint8, 3)
+    _need(absmax, "absmax", absmax.dtype, 3)
+    _need(group_sizes, "group_sizes", torch.int32, 1)
+    _need(group_expert_ids, "group_expert_ids", torch.int32, 1)
+    _need(y, "y", torch.bfloat16, 2)
+    T, K = x.shape
+    M = sorted_slots.numel()
+    E, N, half_k = packed.shape
+    if half_k * 2 != K or absmax.shape != (E, N, K // 64) or y.shape != (M, N):
+        raise ValueError("x/packed/absmax/y shapes do not agree")
+    if G is None:
+        G = min(group_sizes.numel(), M)
+    _check(library().gnf4_grouped_gemm_gather_noalloc(
+        _ptr(x), T, _ptr(sorted_slots), top_k, _ptr(packed), _ptr(absmax), E, N, K,
+        _ptr(group_sizes), _ptr(group_expert_ids), G, M, _ptr(y), path, split_k,
+        _absmax_dtype(absmax), _stream()), "gnf4_grouped_gemm_gather_noalloc")
     return y
 

@@ -486,6 +486,40 @@ gnf4_status gnf4_grouped_gemm_gather(const uint16_t* x, int64_t T, const int32_t
                                      int32_t path, int32_t split_k, int32_t absmax_dtype,
                                      void* stream);
 
+/*
+ * gnf4_grouped_gemm_gather_noalloc -- gnf4_grouped_gemm_gather for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same kernels and
+ * results (bit for bit) as gnf4_grouped_gemm_gather with a workspace of
+ * gnf4_grouped_gemm_workspace_size_ex(M, N, K, G, E, path, split_k) bytes,
+ * but the workspace (split-K partials, staged activation rows) is a
+ * library-owned static array of GNF4_NOALLOC_SCRATCH_BYTES per GPU, which
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (different streams, or host
+ * threads) race and must be ordered by the caller.  Nothing in the array
+ * needs to start cleared.
+ *
+ * Arguments as gnf4_grouped_gemm_gather, without workspace.
+ * Errors: as gnf4_grouped_gemm_gather, plus GNF4_ERR_UNSUPPORTED when the
+ * call needs more workspace than GNF4_NOALLOC_SCRATCH_BYTES (for example a
+ * prefill batch whose staged activation rows exceed it); GNF4_ERR_HIP if the
+ * array's device address cannot be looked up.
+ */
+#define GNF4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+size_t gnf4_noalloc_scratch_bytes(void);
+
+gnf4_status gnf4_grouped_gemm_gather_noalloc(const uint16_t* x, int64_t T,
+                                             const int32_t* sorted_slots, int32_t top_k,
+                                             const uint8_t* packed, const void* absmax, int64_t E,
+                                             int64_t N, int64_t K, const int32_t* group_sizes,
+                                             const int32_t* group_expert_ids, int64_t G,
+                                             int64_t M, uint16_t* y, int32_t path,
+                                             int32_t split_k, int32_t absmax_dtype,
+                                             void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -187,3 +187,26 @@ def test_no_cpu_fallback_in_binding():
     for line in src.splitlines():
         assert "import numpy" not in line
 
+
+def test_noalloc_rejects_bad_arguments(lib):
+    lib.gnf4_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    assert lib.gnf4_noalloc_scratch_bytes() == 32 << 20
+    f = lib.gnf4_grouped_gemm_gather_noalloc
+    # x, T, slots, top_k, packed, absmax, E, N, K, sizes, ids, G, M, y, path, split_k, dtype, stream
+    ok = [FAKE, 4, FAKE, 2, FAKE, FAKE, 4, 64, 128, FAKE, FAKE, 2, 8, FAKE, 0, 0, 1, NULL]
+    bad_slots = list(ok)
+    bad_slots[2] = NULL
+    assert f(*bad_slots) == 1                      # the fused gather needs slots
+    bad_k = list(ok)
+    bad_k[8] = 96
+    assert f(*bad_k) == 1                          # K % 64
+    bad_path = list(ok)
+    bad_path[14] = 3
+    assert f(*bad_path) == 1
+    assert f(*(ok[:12] + [0] + ok[13:])) == 0      # M == 0: nothing to do
+    # a prefill batch whose staged rows exceed the static scratch: refused
+    # before any pointer is touched
+    big = list(ok)
+    big[7], big[8], big[11], big[12], big[14] = 4096, 7168, 256, 32768, 2
+    assert f(*big) == 3
+
