@@ -130,6 +130,61 @@ __device__ __forceinline__ half8 decode8(uint32_t d, const Table& t) {
   return r;
 }
 
+// decode8 as 25 single-instruction micro-steps over explicit state, so a
+// caller can interleave them with other work at instruction grain: step k
+// of the sequence; after step 24, o holds what decode8 returns.
+struct Decode8State {
+  uint32_t ch, cl, t, sl, sh, p1, p2, rl, rh;
+  uint32_t o[4];
+};
+template <int K>
+__device__ __forceinline__ void decode8_step(uint32_t d, const Table& tb, Decode8State& s) {
+  if constexpr (K == 0) s.ch = d >> 4;
+  else if constexpr (K == 1) s.ch &= 0x0f0f0f0fu;
+  else if constexpr (K == 2) s.cl = d & 0x0f0f0f0fu;
+  // high nibbles (the first elements): the four codes of s.ch
+  else if constexpr (K == 3) s.t = s.ch & 0x08080808u;
+  else if constexpr (K == 4) s.sl = s.ch + s.t;
+  else if constexpr (K == 5) s.sh = s.sl ^ 0x10101010u;
+  else if constexpr (K == 6) s.p1 = perm(tb.l1, tb.l0, s.sl);
+  else if constexpr (K == 7) s.p2 = perm(tb.l3, tb.l2, s.sh);
+  else if constexpr (K == 8) s.rl = s.p1 & s.p2;
+  else if constexpr (K == 9) s.p1 = perm(tb.h1, tb.h0, s.sl);
+  else if constexpr (K == 10) s.p2 = perm(tb.h3, tb.h2, s.sh);
+  else if constexpr (K == 11) s.rh = s.p1 & s.p2;
+  else if constexpr (K == 12) s.o[0] = perm(s.rh, s.rl, 0x05010400u);
+  else if constexpr (K == 13) s.o[1] = perm(s.rh, s.rl, 0x07030602u);
+  // low nibbles (the second elements)
+  else if constexpr (K == 14) s.t = s.cl & 0x08080808u;
+  else if constexpr (K == 15) s.sl = s.cl + s.t;
+  else if constexpr (K == 16) s.sh = s.sl ^ 0x10101010u;
+  else if constexpr (K == 17) s.p1 = perm(tb.l1, tb.l0, s.sl);
+  else if constexpr (K == 18) s.p2 = perm(tb.l3, tb.l2, s.sh);
+  else if constexpr (K == 19) s.rl = s.p1 & s.p2;
+  else if constexpr (K == 20) s.p1 = perm(tb.h1, tb.h0, s.sl);
+  else if constexpr (K == 21) s.p2 = perm(tb.h3, tb.h2, s.sh);
+  else if constexpr (K == 22) s.rh = s.p1 & s.p2;
+  else if constexpr (K == 23) s.o[2] = perm(s.rh, s.rl, 0x05010400u);
+  else if constexpr (K == 24) s.o[3] = perm(s.rh, s.rl, 0x07030602u);
+}
+template <int K0, int K1>
+__device__ __forceinline__ void decode8_steps(uint32_t d, const Table& tb, Decode8State& s) {
+  if constexpr (K0 < K1) {
+    decode8_step<K0>(d, tb, s);
+    decode8_steps<K0 + 1, K1>(d, tb, s);
+  }
+}
+constexpr int kDecodeSteps = 25;
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // The stack's scale type names its format: fp32 or bf16 block absmax (NF4),
 // or uint8 E8M0 scales (MXFP4: E2M1 codes, one scale per 32, low nibble
 // first).
@@ -263,20 +318,54 @@ __device__ __forceinline__ void tile_pass(const PassCtx& c) {
       tab = make_table(cok ? ldexpf(ca, -c.sexp) : 0.0f);
     }
     const _Float16* xs = c.s_x + sl * (kPassRows * kLdsRow);
+    // A wavefront's VALU work overlaps only its own matrix-core
+    // instructions (another wavefront's VALU on the same SIMD waits for the
+    // MFMA), so the NF4 decode of sub-step s + 1 is spread over sub-step s's
+    // MFMAs at instruction grain: after each MFMA (32 cycles) come one
+    // fragment read of the next sub-step and about 25 / RT decode
+    // instructions, each group fenced off so the scheduler keeps it there.
+    half8 ax[2][RT];
+    half8 bw[2];
+    auto read_a = [&](int buf, int sub, int rt) {
+      ax[buf][rt] =
+          *reinterpret_cast<const half8*>(xs + (rt * 32 + c.i) * kLdsRow + 64 * c.h + 8 * sub);
+    };
+    if constexpr (kTileMx<AbsT>) {
 #pragma unroll
-    for (int sub = 0; sub < 8; ++sub) {
-      half8 bw;
-      if constexpr (kTileMx<AbsT>)
-        bw = mx_decode8((&cw[0].x)[sub], sub < 4 ? sc0 : sc1);
-      else
-        bw = decode8((&cw[0].x)[sub], tab);
-      half8 ax[RT];
+      for (int sub = 0; sub < 8; ++sub) {
+        bw[0] = mx_decode8((&cw[0].x)[sub], sub < 4 ? sc0 : sc1);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        ax[rt] = *reinterpret_cast<const half8*>(xs + (rt * 32 + c.i) * kLdsRow + 64 * c.h + 8 * sub);
+        for (int rt = 0; rt < RT; ++rt) read_a(0, sub, rt);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[rt], bw, acc[rt], 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[0][rt], bw[0], acc[rt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) read_a(0, 0, rt);
+      bw[0] = decode8(cw[0].x, tab);
+      auto sub_step = [&](auto sub_c) {
+        constexpr int sub = decltype(sub_c)::value;
+        constexpr int cur = sub & 1, nxt = cur ^ 1;
+        Decode8State ds;
+        const uint32_t dn = sub < 7 ? (&cw[0].x)[sub < 7 ? sub + 1 : 0] : 0u;
+        auto group = [&](auto rt_c) {
+          constexpr int rt = decltype(rt_c)::value;
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ax[cur][rt], bw[cur], acc[rt], 0, 0, 0);
+          if constexpr (sub < 7) {
+            read_a(nxt, sub + 1, rt);
+            decode8_steps<rt * kDecodeSteps / RT, (rt + 1) * kDecodeSteps / RT>(dn, tab, ds);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        static_for<RT>(group);
+        if constexpr (sub < 7) {
+          half8 b;
+          __builtin_memcpy(&b, ds.o, sizeof(ds.o));
+          bw[nxt] = b;
+        }
+      };
+      static_for<8>(sub_step);
     }
     if (step < last) {
       store_x(SO{}, 1 - sl);
