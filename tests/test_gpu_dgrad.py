@@ -191,19 +191,22 @@ def test_dgrad_unsplit_fallback_and_determinism():
     check_gemm(u, c["o"], c["written"], "dgrad unsplit")
 
 
-def test_dgrad_dsv3_down_full_size_sampled_rows():
-    """DSV3 down stack (E=256, N=7168 rows reduced, K=2048) with every routed
-    row; the oracle recomputes 24 rows of 3 experts in full."""
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("gemm", ["down", "gate_up"])
+def test_dgrad_dsv3_full_size_sampled_rows(gemm):
+    """DSV3 stacks (down: E=256, N=7168 rows reduced, K=2048; gate_up:
+    N=4096 reduced, K=7168) with every routed row, on the automatic (tile)
+    path; the oracle recomputes up to 24 rows of 3 experts in full."""
     wl = wls.WORKLOADS["dsv3"]
-    K, N = wl.gemm("down")
-    note(f"dgrad full size dsv3/down: generate + pack {wl.E} experts")
-    packed, absmax = device_stack(wl, "down")
+    K, N = wl.gemm(gemm)
+    note(f"dgrad full size dsv3/{gemm}: generate + pack {wl.E} experts")
+    packed, absmax = device_stack(wl, gemm)
     logits = wls.router_logits(wl)
     ref = oracle.ref_route_sort(logits, wl.top_k)
     r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
     gen = torch.Generator(device=DEV).manual_seed(3)
     dy = torch.randn((wl.M, N), device=DEV, generator=gen).to(torch.bfloat16)
-    note("dgrad full size dsv3/down: run")
+    note(f"dgrad full size dsv3/{gemm}: run")
     dx = gnf4.grouped_dgrad(dy, packed, absmax, r.group_sizes, r.group_expert_ids)
     torch.cuda.synchronize()
     groups = oracle.ref_group_rows(ref["group_sizes"], ref["group_expert_ids"], wl.E, wl.M)
@@ -211,7 +214,7 @@ def test_dgrad_dsv3_down_full_size_sampled_rows():
     for gi in rng.choice(len(groups), 3, replace=False):
         _g, e, r0, r1 = groups[gi]
         rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 6)]))
-        p, a = oracle.ref_pack(host_expert(wl, "down", int(e)))
+        p, a = oracle.ref_pack(host_expert(wl, gemm, int(e)))
         w = oracle.ref_unpack(p, a).astype(np.float64)
         idx = torch.from_numpy(rows.astype(np.int64)).to(DEV)
         o = host_f64(dy[idx]) @ w

@@ -5,7 +5,9 @@ seeds), packed by gnf4_pack and multiplied on the automatic path.  The
 oracle gets the same bf16 weights copied back from the generator, packs
 them itself, routes the same logits itself, and computes
   * every output of the decode-sized workloads (M <= 64 rows), and
-  * a sample of outputs, one by one, of the DeepSeek-V3-sized prefill.
+  * for the DeepSeek-V3-sized prefill, every output of four complete groups
+    (the first, last, largest and smallest) and a sample of outputs, one by
+    one, across 48 more.
 """
 
 import numpy as np
@@ -33,6 +35,13 @@ def device_stack(wl, gemm, layer=0):
 
 def host_expert(wl, gemm, e, layer=0):
     return wls.expert_weights_device(wl, gemm, e, DEV, layer).float().cpu().numpy()
+
+
+def complete_groups(groups):
+    """The first, last, largest and smallest of the groups that write rows."""
+    sizes = [r1 - r0 for (_g, _e, r0, r1) in groups]
+    pick = {0, len(groups) - 1, int(np.argmax(sizes)), int(np.argmin(sizes))}
+    return [groups[i] for i in sorted(pick)]
 
 
 @pytest.mark.parametrize("name", ["olmoe", "qwen3_t1", "qwen3_t8", "gptoss"])
@@ -66,6 +75,7 @@ def test_decode_workload_full_stack(name, gemm):
     check_gemm(y, y_ref, written, f"{name}/{gemm} full size")
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("gemm", ["gate_up", "down"])
 def test_dsv3_prefill_sampled(gemm):
     wl = wls.WORKLOADS["dsv3"]
@@ -119,3 +129,12 @@ def test_dsv3_prefill_sampled(gemm):
             expect[i] = float(np.dot(x_host[rows[i]].astype(np.float64), wt[row_of[int(cols[i])]]))
     rms = float(np.sqrt(np.mean(expect ** 2)))
     check_entries(yh[rows, cols], expect, rms, f"dsv3/{gemm} sampled")
+
+    # every output of four complete groups: first, last, largest, smallest
+    for g, e, r0, r1 in complete_groups(groups):
+        note(f"full-size dsv3/{gemm}: group {g} (expert {e}, {r1 - r0} rows) in full")
+        p, a = oracle.ref_pack(host_expert(wl, gemm, int(e)))
+        wt = oracle.ref_unpack(p, a).astype(np.float64)
+        o = x_host[r0:r1].astype(np.float64) @ wt.T
+        check_gemm(y[r0:r1], o, np.ones(r1 - r0, bool),
+                   f"dsv3/{gemm} group {g} (expert {e}, {r1 - r0} rows)")

@@ -18,6 +18,7 @@ import oracle
 from grouped_nf4_expert_amd import gnf4
 from grouped_nf4_expert_amd import workloads as wls
 
+from test_gpu_full_size import complete_groups
 from gpu_util import DEV, bf16_dev, check_gemm, host_f64, note
 from test_gpu_gemm import BOUNDARY_CASES
 
@@ -233,12 +234,14 @@ def test_mxfp4_tile_activation_magnitudes(scale):
     assert np.all(host_f64(y)[7] == 0.0)
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("gemm", ["gate_up", "down"])
 def test_mxfp4_dsv3_prefill_sampled(gemm):
     """DeepSeek-V3-shaped prefill (E=256, T=4096, k=8) over a random MXFP4
     stack on the automatic path (every group on the tile path) with the fused
-    gather; run twice (deterministic); the oracle recomputes sampled outputs
-    of 48 groups plus every 64th column of the first and last rows."""
+    gather; run twice (deterministic); the oracle recomputes every output of
+    four complete groups (first, last, largest, smallest), sampled outputs of
+    48 more groups and every 64th column of the first and last rows."""
     wl = wls.WORKLOADS["dsv3"]
     K, N = wl.gemm(gemm)
     note(f"mxfp4 full-size dsv3/{gemm}: stack E={wl.E} N={N} K={K}")
@@ -278,3 +281,10 @@ def test_mxfp4_dsv3_prefill_sampled(gemm):
     rms = float(np.sqrt(np.mean(expect ** 2)))
     bad = np.abs(got - expect) > 8e-3 * np.abs(expect) + 1e-3 * rms
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} sampled outputs outside tolerance"
+    # every output of four complete groups: first, last, largest, smallest
+    for g, e, r0, r1 in complete_groups(groups):
+        note(f"mxfp4 full-size dsv3/{gemm}: group {g} (expert {e}, {r1 - r0} rows) in full")
+        wt = oracle.ref_mx_unpack(packed[e].cpu().numpy(), scales[e].cpu().numpy())
+        xr = x_tok[ref["sorted_slots"][r0:r1] // wl.top_k].astype(np.float64)
+        check_gemm(y[r0:r1], xr @ np.asarray(wt, np.float64).T, np.ones(r1 - r0, bool),
+                   f"mxfp4 dsv3/{gemm} group {g} (expert {e}, {r1 - r0} rows)")
