@@ -4,7 +4,9 @@
 
 Each translation unit is compiled with hipcc for gfx950 only, in parallel,
 then linked into one shared library next to this file.  Packed fp32 VALU
-instructions are disabled for every device compile.
+instructions are disabled for every device compile.  The machine-ceiling
+probes (ceilings.hip, include/gnf4_ceilings.h) are linked into a library of
+their own, libgnf4_ceilings.so, which the GEMM library does not use.
 """
 
 import os
@@ -21,6 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgnf4.so")
 SOURCES = ["api.hip", "pack.hip", "route.hip", "gather.hip", "decode.hip", "tile.hip",
            "glue.hip", "dgrad.hip", "validate.hip"]
+CEIL_SOURCES = ["ceilings.hip"]
+CEIL_LIB = os.path.join(PKG, "libgnf4_ceilings.so")
 ARCH = "gfx950"
 
 
@@ -40,27 +44,40 @@ def common_flags():
     ]
 
 
+# Per-source flags.  decode.hip: its kernels take their first scalar
+# arguments preloaded into SGPRs at wavefront launch (gfx950 kernel-argument
+# preloading), so the first dependent loads need no argument-segment read.
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=7"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEIL_LIB}")
     return LIB
 
 

@@ -36,6 +36,7 @@
 //    order (deterministic).
 
 #include <limits.h>
+#include <stddef.h>
 
 #include <type_traits>
 
@@ -62,14 +63,26 @@ constexpr int kMaxLoads = 4;    // weight chunks in flight per lane (NU * steps)
 constexpr int kMaxSteps = 4;
 
 struct DecodeKArgs {
-  GemmArgs g;
-  int S, cps, cpr, rows_per_block;
+  // What every wavefront reads before its weight loads, first and packed
+  // (80 bytes: with the 44 bytes of preloaded leading arguments, two 64-byte
+  // lines of the argument segment); copies of fields of g.
+  const uint16_t* x;
+  const uint8_t* packed;
+  const void* absmax;
+  void* out;  // y (bf16 bits) when S == 1, else the fp32 split partials
   double inv_slot_div;  // 1 / slot_div, for the fused gather's row index
+  int N, K, T, slot_div, rows_max_decode;
+  int S, cps, cpr, rows_per_block;
+  int route_k;  // picks per token of the routed launch (ro.K)
+  // the rest: the split-K reduce's arguments and the route/sort outputs,
+  // which only workgroup (0, 0, 0) of the routed launch writes
+  GemmArgs g;
   // Routing folded into the launch (one token, E <= 64): the router logits
   // [E] and the route/sort outputs that workgroup (0, 0, 0) writes.
   const float* route_logits;
   RouteOneOut ro;
 };
+static_assert(offsetof(DecodeKArgs, g) == 80, "the hot arguments fill 80 bytes at the front");
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* out) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
@@ -241,6 +254,17 @@ __device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
   return q;
 }
 
+// Every kernel argument the decode kernel reads before its weight loads, in
+// SGPRs at this point: the compiler would otherwise read each from the
+// argument segment where first used, one dependent round trip at a time.
+// Only what the kernel uses: each further line of the segment costs a read.
+__device__ __forceinline__ void pin_args(const DecodeKArgs& a) {
+  asm volatile("" ::"s"(a.x), "s"(a.packed), "s"(a.absmax), "s"(a.out), "s"(a.inv_slot_div),
+               "s"(a.N), "s"(a.K), "s"(a.T), "s"(a.slot_div), "s"(a.rows_max_decode), "s"(a.S),
+               "s"(a.cps), "s"(a.cpr), "s"(a.rows_per_block), "s"(a.route_k)
+               : "memory");
+}
+
 // The terms of one weight dword (8 codes, 4 bytes; a byte's high nibble is
 // its first element) against its 8 activations of R rows, added to pr.
 template <int R, typename AbsT>
@@ -294,69 +318,82 @@ __device__ __forceinline__ void dword_terms(uint32_t d, const float (&xw)[R][8],
 // the weights in the same order.
 // ROUTED = 0: groups from sizes/ids; 1 or 2: a single token routed in the
 // launch, over up to 64 * ROUTED experts (ROUTED router entries per lane).
+//
+// The first loads (router logits, or group sizes / ids and the slot table)
+// need only the leading scalar arguments, which the library builds with
+// kernel-argument preloading: they arrive in SGPRs at wavefront launch, so
+// those loads are issued before any read of the argument segment, and every
+// other argument is read in one batch while they are in flight (pin_args)
+// rather than a round trip at a time where first used.
 template <int L, int NU, int R, int STEPS, typename AbsT, int ROUTED = 0>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const int32_t* __restrict__ k_sizes, const int32_t* __restrict__ k_ids,
+    const int32_t* __restrict__ k_slots, const float* __restrict__ k_logits, int k_G, int k_M,
+    int k_E, DecodeKArgs a) {
   // 16 levels at an 8-byte stride, at a fixed LDS address so a code's byte
   // offset is the whole address (no per-read base add)
   __shared__ float s_lut[32];
   extern __shared__ float4 s_x[];
   constexpr int RPW = kWave / L;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const bool gather = a.g.slots != nullptr;
-  const bool slots_in_lanes = gather && a.g.M <= kWave;
+  const bool gather = k_slots != nullptr;
+  const bool slots_in_lanes = gather && k_M <= kWave;
   // (1) metadata: the slot table (issued first, independent of the group)
   // and the group this workgroup serves
   int my_slot = 0;
   GroupRef gr;
   if constexpr (ROUTED > 0) {
     // One token routed in the launch.  Entry s of lane l holds expert
-    // l + 64 s's key, as the route/sort kernels build it (rank_token); its
-    // rank, the number of larger keys, is counted by the wavefronts together,
-    // each against the keys of 64 / kWaves of the lanes, and summed through
-    // LDS: the same integers rank_token gives.  Group j is the j-th pick in
-    // expert order, one row (row j, token 0).
+    // l + 64 s's key, as the route/sort kernels build it (rank_token): the
+    // logit's order-preserving key above the complemented expert id, so keys
+    // are distinct, larger is better and the lower id wins a tie.  Every
+    // wavefront finds the K-th largest key on its own, bit by bit from the
+    // top (a radix select over ballot counts: the largest t with at least K
+    // keys >= t); the picks are the keys >= t, the same set rank_token's
+    // ranks < K give.  Only the bits that differ between keys are searched:
+    // the 32 of the logit's key, then the low 7 of the id part (ids below
+    // 128 share bits 7..31 of ~id).  Group j is the j-th pick in expert order,
+    // one row (row j, token 0).
     constexpr int EPL = ROUTED;
-    constexpr int kKeys = kWave / kWaves;
-    static_assert(kKeys * kWaves == kWave, "the keys split evenly over the wavefronts");
-    __shared__ int s_part[kWaves][EPL][kWave];
-    const int E = a.ro.E;
+    const int E = k_E;
     float val[EPL];
-    int rank[EPL];
     uint64_t key[EPL];
 #pragma unroll
     for (int s = 0; s < EPL; ++s) {
       const int e = lane + kWave * s;
-      val[s] = e < E ? a.route_logits[e] : 0.0f;
+      val[s] = e < E ? k_logits[e] : 0.0f;
+    }
+    pin_args(a);
+    const int kpick = a.route_k;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) {
+      const int e = lane + kWave * s;
       key[s] = e < E ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
                      : 0ull;
     }
-    int part[EPL];
+    uint64_t t = 0;
+    auto try_bit = [&](int b) {
+      const uint64_t cand = t | (1ull << b);
+      int cnt = 0;
 #pragma unroll
-    for (int s = 0; s < EPL; ++s) part[s] = 0;
+      for (int s = 0; s < EPL; ++s) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[s] >= cand));
+      if (cnt >= kpick) t = cand;
+    };
 #pragma unroll
-    for (int s2 = 0; s2 < EPL; ++s2)
+    for (int b = 63; b >= 32; --b) try_bit(b);
+    t |= 0xffffff80ull;
 #pragma unroll
-      for (int q = 0; q < kKeys; ++q) {
-        const uint64_t kj = readlane64(key[s2], kKeys * wave + q);
+    for (int b = 6; b >= 0; --b) try_bit(b);
+    uint64_t sel[EPL];
 #pragma unroll
-        for (int s = 0; s < EPL; ++s) part[s] += kj > key[s] ? 1 : 0;
-      }
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) s_part[wave][s][lane] = part[s];
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) {
-      rank[s] = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) rank[s] += s_part[w][s][lane];
-    }
+    for (int s = 0; s < EPL; ++s) sel[s] = __builtin_amdgcn_ballot_w64(key[s] >= t);
     // the j-th pick in expert order (entry 0 of every lane, then entry 1)
     const int j = blockIdx.y;
     int jj = j;
     gr.expert = 0;
 #pragma unroll
     for (int s = 0; s < EPL; ++s) {
-      uint64_t m = __ballot(rank[s] < a.ro.K);
+      uint64_t m = sel[s];
       const int c = __popcll(m);
       if (jj >= 0 && jj < c) {  // uniform
         for (int q = 0; q < jj; ++q) m &= m - 1;
@@ -367,22 +404,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     gr.g = j;
     gr.size = 1;
     gr.row = j;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0)
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0) {
+      // the route/sort outputs need each pick's rank: the picks above it
+      int rank[EPL];
+#pragma unroll
+      for (int s = 0; s < EPL; ++s) rank[s] = 0;
+#pragma unroll
+      for (int s2 = 0; s2 < EPL; ++s2)
+        for (uint64_t m = sel[s2]; m; m &= m - 1) {
+          const uint64_t kj = readlane64(key[s2], __ffsll((unsigned long long)m) - 1);
+#pragma unroll
+          for (int s = 0; s < EPL; ++s) rank[s] += kj > key[s] ? 1 : 0;
+        }
+#pragma unroll
+      for (int s = 0; s < EPL; ++s)
+        if (!((sel[s] >> lane) & 1)) rank[s] = kpick;
       route_one_token_write<EPL>(a.ro, lane, val, rank);
+    }
   } else {
-    if (slots_in_lanes && lane < a.g.M) my_slot = a.g.slots[lane];
-    if (!find_group(a.g.sizes, a.g.ids, a.g.G, a.g.E, a.g.M, 1, a.g.rows_max_decode, blockIdx.y,
-                    gr))
+    if (slots_in_lanes && lane < k_M) my_slot = k_slots[lane];
+    GroupChunk first;
+    load_group_chunk(k_sizes, k_ids, k_G, 0, first);
+    pin_args(a);
+    if (!find_group_from(k_sizes, k_ids, k_G, k_E, k_M, 1, a.rows_max_decode, blockIdx.y, first,
+                         gr))
       return;
   }
   const int s = blockIdx.z;
   const int team = lane / L, tl = lane % L;
-  const int N = a.g.N, K = a.g.K;
+  const int N = a.N, K = a.K;
   const int n_base = blockIdx.x * a.rows_per_block + wave * (RPW * NU) + team * NU;
   const size_t row_bytes = (size_t)K / 2;
   const int bpr = K / kBlock;
-  const uint8_t* wexp = a.g.packed + (size_t)gr.expert * N * row_bytes;
-  const AbsT* aexp = static_cast<const AbsT*>(a.g.absmax) +
+  const uint8_t* wexp = a.packed + (size_t)gr.expert * N * row_bytes;
+  const AbsT* aexp = static_cast<const AbsT*>(a.absmax) +
                     (size_t)gr.expert * N * (kMxfp4<AbsT> ? 2 * bpr : bpr);
   const int c_begin = s * a.cps;
   const int c_end = min(c_begin + a.cps, a.cpr);
@@ -393,8 +448,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   const float* lut = s_lut;
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const int r_begin = gr.row;
-  const int r_end = min(r_begin + gr.size, a.g.M);
-  const int slot_lim = a.g.T * a.g.slot_div;
+  const int r_end = min(r_begin + gr.size, k_M);
+  const int slot_lim = a.T * a.slot_div;
 
   // source activation row of each of the R rows of a chunk (-1: skip)
   int xrow[R];
@@ -408,8 +463,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
         continue;
       }
       if (gather && row < r_end) {
-        const int slot = slots_in_lanes ? __builtin_amdgcn_readlane(my_slot, row) : a.g.slots[row];
-        xrow[r] = (slot >= 0 && slot < slot_lim) ? div_slot(slot, a.g.slot_div, a.inv_slot_div) : -1;
+        const int slot = slots_in_lanes ? __builtin_amdgcn_readlane(my_slot, row) : k_slots[row];
+        xrow[r] = (slot >= 0 && slot < slot_lim) ? div_slot(slot, a.slot_div, a.inv_slot_div) : -1;
       }
     }
   };
@@ -418,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   rows_of(r_begin);
   XStage<R, x_batch(R, L, STEPS)> stage;
   stage.init(c_begin, ncs);
-  stage.load(a.g.x, K, xrow, 0);
+  stage.load(a.x, K, xrow, 0);
   uint4 wq[STEPS][NU];
   float av[STEPS][NU];
 #pragma unroll
@@ -503,9 +558,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
         const int row = r0 + r;
         if (xrow[r] < 0) continue;
         if (a.S == 1)
-          a.g.y[(size_t)row * N + n] = f32_to_bf16(acc[j][r]);
+          static_cast<uint16_t*>(a.out)[(size_t)row * N + n] = f32_to_bf16(acc[j][r]);
         else
-          a.g.partial[((size_t)s * a.g.M + row) * N + n] = acc[j][r];
+          static_cast<float*>(a.out)[((size_t)s * k_M + row) * N + n] = acc[j][r];
       }
     }
   };
@@ -518,7 +573,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   for (int r0 = r_begin + R; r0 < r_end; r0 += R) {
     lds_barrier();  // every wavefront is done with the previous chunk
     rows_of(r0);
-    stage.all(a.g.x, K, xrow, s_x);
+    stage.all(a.x, K, xrow, s_x);
     lds_barrier();
     chunk(r0);
   }
@@ -553,7 +608,8 @@ hipError_t launch_one(const DecodeKArgs& a, const DecodePlan& p, hipStream_t str
   const dim3 grid((unsigned)p.n_tiles, (unsigned)group_slots(a.g.G, a.g.M, 1), (unsigned)p.S);
   const size_t lds = (size_t)R * (size_t)(p.cps + 1) * 128;
   hipLaunchKernelGGL((decode_kernel<L, NU, R, STEPS, AbsT, ROUTED>), grid, dim3(kThreads), lds,
-                     stream, a);
+                     stream, a.g.sizes, a.g.ids, a.g.slots, a.route_logits, a.g.G, a.g.M,
+                     ROUTED > 0 ? a.ro.E : a.g.E, a);
   return hipGetLastError();
 }
 
@@ -703,6 +759,16 @@ size_t decode_workspace_bytes(const DecodePlan& p, int64_t M, int64_t N) {
 static DecodeKArgs decode_args(const GemmArgs& g, const DecodePlan& p) {
   DecodeKArgs a;
   a.g = g;
+  a.x = g.x;
+  a.packed = g.packed;
+  a.absmax = g.absmax;
+  a.out = p.S == 1 ? static_cast<void*>(g.y) : static_cast<void*>(g.partial);
+  a.N = g.N;
+  a.K = g.K;
+  a.T = g.T;
+  a.slot_div = g.slot_div;
+  a.rows_max_decode = g.rows_max_decode;
+  a.route_k = 0;
   a.S = p.S;
   a.cps = p.cps;
   a.cpr = g.K / 32;
@@ -725,6 +791,7 @@ hipError_t launch_decode_routed(const GemmArgs& g, const DecodePlan& p, const fl
   DecodeKArgs a = decode_args(g, p);
   a.route_logits = logits;
   a.ro = ro;
+  a.route_k = ro.K;
   if (ro.E > 2 * kWave) return hipErrorInvalidValue;
   const bool two = ro.E > kWave;
   hipError_t err;

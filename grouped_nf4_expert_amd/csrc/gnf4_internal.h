@@ -136,18 +136,36 @@ struct GroupRef {
 // wavefront's partial sums fit an int) and the running row count saturates at
 // M, where nothing is written.  All loads of a 256-group chunk are issued
 // before any is used.
-__device__ __forceinline__ bool find_group(const int32_t* sizes, const int32_t* ids, int G,
-                                           int E, int M, int lo, int hi, int j, GroupRef& out) {
+// The loads of one 256-group chunk of find_group, starting at group c0.
+struct GroupChunk {
+  int sv[4], ev[4];
+};
+__device__ __forceinline__ void load_group_chunk(const int32_t* sizes, const int32_t* ids, int G,
+                                                 int c0, GroupChunk& ch) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = c0 + q * kWave + lane;
+    ch.sv[q] = i < G ? sizes[i] : 0;
+    ch.ev[q] = i < G ? ids[i] : -1;
+  }
+}
+
+// find_group with the first chunk's loads already issued (load_group_chunk
+// at c0 = 0), so a kernel can put other work between issue and use.
+__device__ __forceinline__ bool find_group_from(const int32_t* sizes, const int32_t* ids, int G,
+                                                int E, int M, int lo, int hi, int j,
+                                                const GroupChunk& first, GroupRef& out) {
   const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   int seen = 0, rows = 0;
   for (int c0 = 0; c0 < G; c0 += 4 * kWave) {
-    int sv[4], ev[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = c0 + q * kWave + lane;
-      sv[q] = i < G ? sizes[i] : 0;
-      ev[q] = i < G ? ids[i] : -1;
-    }
+    GroupChunk ch;
+    if (c0 == 0)
+      ch = first;
+    else
+      load_group_chunk(sizes, ids, G, c0, ch);
+    const int* sv = ch.sv;
+    const int* ev = ch.ev;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool ok = sv[q] >= lo && sv[q] <= hi && ev[q] >= 0 && ev[q] < E;
@@ -171,6 +189,13 @@ __device__ __forceinline__ bool find_group(const int32_t* sizes, const int32_t* 
     }
   }
   return false;
+}
+
+__device__ __forceinline__ bool find_group(const int32_t* sizes, const int32_t* ids, int G,
+                                           int E, int M, int lo, int hi, int j, GroupRef& out) {
+  GroupChunk first;
+  load_group_chunk(sizes, ids, G, 0, first);
+  return find_group_from(sizes, ids, G, E, M, lo, hi, j, first, out);
 }
 
 // Upper bound on the groups with at least `lo` rows that start inside M
