@@ -50,32 +50,35 @@ def common_flags():
 EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=7"]}
 
 
-def _compile(src):
+def _compile(src, extra=()):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-           "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def _link(objs, lib):
+def _link(objs, lib, extra=()):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
 
 
-def build(verbose=False):
+def build(verbose=False, extra_compile=(), extra_link=()):
+    """Compile every source and link both libraries.  extra_compile /
+    extra_link: further hipcc flags (build_sanitized.py passes host-only
+    sanitizer flags)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + CEIL_SOURCES
     with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
-        objs = dict(zip(srcs, ex.map(_compile, srcs)))
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB)
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra_compile), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, extra_link)
+    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB, extra_link)
     if verbose:
         print(f"built {LIB} and {CEIL_LIB}")
     return LIB
