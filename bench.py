@@ -21,8 +21,9 @@ reported, with the worst beside it, and the CPU oracle is timed on a
 bounded sample of the same workload.
 
 Printed: ONE JSON line.  Other modes (--cells/--dgrad/--mxfp4/--glue JSONL
-files, --dominant-only and --copy-mb for counter collection, --summarize
-for rocprofv3 CSV output) run in this process.
+files, --ceilings for the machine ceilings, --dominant-only and --copy-mb
+for counter collection, --summarize for rocprofv3 CSV output) run in this
+process.
 """
 
 import argparse
@@ -81,10 +82,14 @@ def parse():
                     help="time the grouped dgrad alone at each workload's shapes into this JSONL")
     ap.add_argument("--glue", default="",
                     help="time the SwiGLU and top-k combine kernels alone into this JSONL")
+    ap.add_argument("--ceilings", default="",
+                    help="measure the machine ceilings (pure-read GB/s against size, empty "
+                         "launch, matrix-core clock, vendor fp16 GEMM) into this JSONL")
     ap.add_argument("--absmax-dtype", choices=("f32", "bf16"), default="f32",
                     help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
     ap.add_argument("--only", default="",
-                    help="comma-separated workload names: restrict --cells / --mxfp4 / --dgrad to them")
+                    help="comma-separated workload names: restrict --cells / --mxfp4 / --dgrad to "
+                         "them (--cells also takes workload/gemm, e.g. dsv3/down)")
     ap.add_argument("--unfused-route", action="store_true",
                     help="run the route/sort as its own launch even where it folds into gate_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -274,13 +279,19 @@ def time_cells(dev, names=CELL_NAMES, path=None, min_decode=100, min_prefill=10)
     out = open(path, "w") if path else None
     recs = []
     stack_cache = {}
-    for name in names:
+    chosen = {}  # workload -> the GEMMs asked for ("dsv3" = both, "dsv3/down" = one)
+    for n in names:
+        w, _, g = n.partition("/")
+        chosen.setdefault(w, set()).add(g or "*")
+    for name, gemms in chosen.items():
         wl = wls.WORKLOADS[name]
         r = gnf4.route_sort(torch.from_numpy(wls.router_logits(wl)).to(dev), wl.top_k)
         G = min(wl.E, wl.M)
         ng = int(r.num_groups.cpu()[0])
         prefill = wl.M >= 32 * G  # the automatic path: every group on the tile path
         for gemm in ("gate_up", "down"):
+            if "*" not in gemms and gemm not in gemms:
+                continue
             K, N = wl.gemm(gemm)
             rot, copies = cell_plan(wl.E, ng, N, K)
             key = (wl.E, N, K)
@@ -501,6 +512,171 @@ def time_mxfp4(path, dev, only=()):
         del stacks
         torch.cuda.empty_cache()
     out.close()
+
+
+def ceilings_library():
+    import ctypes
+    path = os.path.join(ROOT, "grouped_nf4_expert_amd", "libgnf4_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m grouped_nf4_expert_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.gnf4_ceil_read.argtypes = [vp, ctypes.c_size_t, ci, vp, vp]
+    lib.gnf4_ceil_empty.argtypes = [ci, vp]
+    lib.gnf4_ceil_mfma.argtypes = [ci, ci, vp, vp, vp]
+    for f in (lib.gnf4_ceil_read, lib.gnf4_ceil_empty, lib.gnf4_ceil_mfma):
+        f.restype = ci
+    return lib
+
+
+READ_SIZES_MIB = (1, 2, 4, 9, 18, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+READ_BLOCKS = (256, 512, 1024, 2048, 4096, 8192)
+
+
+def measure_ceilings(path, dev, replays=5):
+    """The limits the kernels' fractions are read against, on this GPU.
+
+    * pure read: each size S (MiB) is read by one launch of a streaming
+      kernel; back-to-back launches in a HIP graph cycle over copies at
+      distinct addresses (at least 1 GiB in all, past the 256 MB Infinity
+      Cache), best over READ_BLOCKS grid sizes; 9 and 18 MiB are the weight
+      bytes one OLMoE-shaped down / gate_up decode launch reads.
+    * empty launch: per-launch time of 1000 back-to-back empty kernels.
+    * matrix cores: a v_mfma_f32_32x32x16_f16 loop on every SIMD, its
+      TFLOP/s by HIP events and its shader clock from each wave's
+      s_memtime / s_memrealtime.
+    * vendor fp16 GEMM (hipBLASLt through torch): 8192^3 and the
+      DeepSeek-V3 expert shapes as a batch of 256 equal 128-row groups."""
+    import ctypes
+    import torch
+    lib = ceilings_library()
+    out = open(path, "w") if path else None
+    recs = []
+
+    def emit(rec):
+        recs.append(rec)
+        if out:
+            out.write(json.dumps(rec) + "\n")
+            out.flush()
+        print(f"[ceiling] {json.dumps(rec)}", file=sys.stderr, flush=True)
+
+    def st():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ok(status, what):
+        if status != 0:
+            raise RuntimeError(f"{what}: status {status}")
+
+    def timed(graph, launches):
+        graph.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(replays)]
+        for a, b in evs:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 / launches for a, b in evs)
+        return us[len(us) // 2]
+
+    big = 4 << 30
+    buf = torch.randint(0, 256, (big,), dtype=torch.uint8, device=dev)
+    xor_out = torch.empty(max(READ_BLOCKS), dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    for mib in READ_SIZES_MIB:
+        S = mib << 20
+        copies = min(max(1, -(-(1 << 30) // S)), big // S)
+        best = None
+        for blocks in READ_BLOCKS:
+            if blocks != READ_BLOCKS[0] and blocks * 256 > S // 16:
+                break  # threads past one word each would sit idle
+
+            def launches(blocks=blocks):
+                for c in range(copies):
+                    ok(lib.gnf4_ceil_read(ctypes.c_void_p(base + c * S), S, blocks,
+                                          ctypes.c_void_p(xor_out.data_ptr()), st()), "read")
+            g = capture(launches)
+            us = timed(g, copies)
+            del g
+            if best is None or us < best[0]:
+                best = (us, blocks)
+        check = None
+        if S <= (64 << 20):  # every word read: the XOR of the block outputs is the buffer's
+            ok(lib.gnf4_ceil_read(ctypes.c_void_p(base), S, best[1],
+                                  ctypes.c_void_p(xor_out.data_ptr()), st()), "read")
+            torch.cuda.synchronize()
+            host = buf[:S].cpu().numpy().view(np.uint32)
+            want = int(np.bitwise_xor.reduce(host))
+            got = int(np.bitwise_xor.reduce(xor_out[:best[1]].cpu().numpy().view(np.uint32)))
+            check = got == want
+            assert check, f"read probe at {mib} MiB missed words"
+        emit({"ceiling": "pure_read", "MiB": mib, "us": round(best[0], 3),
+              "GBps": round(S / best[0] / 1e3, 1), "frac_of_8TBps": round(S / best[0] / 8e6, 4),
+              "blocks": best[1], "copies_cycled": copies, "xor_check": check})
+    del buf, xor_out
+    torch.cuda.empty_cache()
+
+    for blocks in (1, 2048):
+        n = 1000
+
+        def empties(blocks=blocks):
+            for _ in range(n):
+                ok(lib.gnf4_ceil_empty(blocks, st()), "empty")
+        g = capture(empties)
+        emit({"ceiling": "empty_launch", "blocks": blocks, "threads": 64,
+              "us_per_launch": round(timed(g, n), 3), "launches_per_replay": n})
+        del g
+
+    for blocks, iters in ((1024, 200000), (2048, 100000)):
+        waves = blocks * 4
+        stamps = torch.zeros(waves * 4, dtype=torch.int64, device=dev)
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        evs = []
+        for _ in range(3):  # the last of three back-to-back runs: clocks settled
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ok(lib.gnf4_ceil_mfma(iters, blocks, ctypes.c_void_p(stamps.data_ptr()),
+                                  ctypes.c_void_p(sink.data_ptr()), st()), "mfma")
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = evs[-1][0].elapsed_time(evs[-1][1])
+        t = stamps.cpu().numpy().reshape(waves, 4).astype(np.float64)
+        wave_s = (t[:, 3] - t[:, 2]) / 100e6
+        ghz = float(np.median((t[:, 1] - t[:, 0]) / wave_s) / 1e9)
+        flops = float(waves) * iters * 4 * 32768
+        emit({"ceiling": "mfma_f16_32x32x16", "blocks": blocks, "waves_per_simd": waves // 1024,
+              "iters": iters, "ms": round(ms, 3), "TFLOPs": round(flops / ms / 1e9, 1),
+              "frac_of_2500": round(flops / ms / 1e9 / MFMA_FP16_PEAK_TFLOPS, 4),
+              "shader_clock_GHz_median": round(ghz, 3),
+              "longest_wave_vs_event": round(float(wave_s.max()) * 1e3 / ms, 4),
+              "peak_at_clock_TFLOPs": round(1024 * 32768 / 32 * ghz / 1e3, 1)})
+        del stamps, sink
+
+    gen = torch.Generator(device=dev).manual_seed(7)
+    cases = [("square", 1, 8192, 8192, 8192),
+             ("dsv3_gate_up_256x128", 256, 128, 7168, 4096),
+             ("dsv3_down_256x128", 256, 128, 2048, 7168)]
+    for name, B, Mr, K, N in cases:
+        a = torch.randn((B, Mr, K), device=dev, generator=gen).to(torch.float16)
+        b = torch.randn((B, K, N), device=dev, generator=gen).to(torch.float16).contiguous()
+        c = torch.empty((B, Mr, N), device=dev, dtype=torch.float16)
+
+        def gemm():
+            torch.bmm(a, b, out=c)
+        g = capture(gemm)
+        us = timed(g, 1)
+        del g
+        fl = 2.0 * B * Mr * K * N
+        emit({"ceiling": "vendor_fp16_gemm", "case": name, "batch": B, "M": Mr, "K": K,
+              "N": N, "us": round(us, 1), "TFLOPs": round(fl / us / 1e6, 1),
+              "frac_of_2500": round(fl / us / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4)})
+        del a, b, c
+        torch.cuda.empty_cache()
+    if out:
+        out.close()
+    return recs
 
 
 def time_glue(path, dev, reps=10):
@@ -896,7 +1072,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     special = (args.glue or args.cells or args.dgrad or args.mxfp4 or args.copy_mb or
-               args.dominant_only)
+               args.dominant_only or args.ceilings)
     if not special and not args.child:
         parent_main(args)
         return
@@ -912,6 +1088,9 @@ def main():
     only = tuple(w for w in args.only.split(",") if w)
     if args.glue:
         time_glue(args.glue, dev)
+        return
+    if args.ceilings:
+        measure_ceilings(args.ceilings, dev)
         return
     if args.cells:
         time_cells(dev, only or CELL_NAMES, args.cells)
