@@ -555,6 +555,77 @@ gnf4_status gnf4_route_gemm_one_token(const float* logits, int64_t E, int32_t to
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
+size_t gnf4_moe_ffn_one_token_workspace_size(int32_t top_k) {
+  if (top_k < 1) return 0;
+  return ffn_sync_bytes(top_k);
+}
+
+gnf4_status gnf4_moe_ffn_one_token(const float* logits, int64_t E, int32_t top_k,
+                                   const uint16_t* x, const uint8_t* gate_up_packed,
+                                   const void* gate_up_absmax, const uint8_t* down_packed,
+                                   const void* down_absmax, int32_t absmax_dtype, int64_t H,
+                                   int64_t I, uint16_t* h, uint16_t* y, int32_t* topk_ids,
+                                   float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                                   int32_t* slot_rows, int32_t* group_sizes,
+                                   int32_t* group_expert_ids, int32_t* num_groups,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (E < 1 || top_k < 1 || top_k > E || H < kBlock || H % kBlock != 0 || I < kBlock ||
+      I % kBlock != 0)
+    return GNF4_ERR_INVALID_ARG;
+  if (E > 128 || top_k > 32) return GNF4_ERR_UNSUPPORTED;
+  if (2 * I * (H / 2) >= ((int64_t)1 << 31) || H * (I / 2) >= ((int64_t)1 << 31) ||
+      E * 2 * I >= ((int64_t)1 << 31) || E * H >= ((int64_t)1 << 31))
+    return GNF4_ERR_UNSUPPORTED;
+  if (!valid_dtype(absmax_dtype)) return GNF4_ERR_INVALID_ARG;
+  const void* out4[] = {topk_ids, topk_w, expert_offsets, sorted_slots, group_sizes,
+                        group_expert_ids, num_groups, logits};
+  for (const void* p : out4)
+    if (!p || !aligned(p, 4)) return GNF4_ERR_INVALID_ARG;
+  if (!x || !gate_up_packed || !gate_up_absmax || !down_packed || !down_absmax || !h || !y)
+    return GNF4_ERR_INVALID_ARG;
+  const size_t ab = dtype_bytes(absmax_dtype);
+  if (!aligned(x, 16) || !aligned(gate_up_packed, 16) || !aligned(down_packed, 16) ||
+      !aligned(gate_up_absmax, ab) || !aligned(down_absmax, ab) || !aligned(h, 16) ||
+      !aligned(y, 2) || (slot_rows && !aligned(slot_rows, 4)))
+    return GNF4_ERR_INVALID_ARG;
+  const size_t need = gnf4_moe_ffn_one_token_workspace_size(top_k);
+  if (!workspace || workspace_bytes < need) return GNF4_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return GNF4_ERR_INVALID_ARG;
+  for (const void* p : out4)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  const void* more[] = {x, gate_up_packed, gate_up_absmax, down_packed, down_absmax, h, y,
+                        workspace};
+  for (const void* p : more)
+    if (!is_device_ptr(p)) return GNF4_ERR_NOT_DEVICE_PTR;
+  if (slot_rows && !is_device_ptr(slot_rows)) return GNF4_ERR_NOT_DEVICE_PTR;
+  FfnPlan plan;
+  if (!plan_ffn(E, top_k, H, I, device_cu_count(), plan)) return GNF4_ERR_UNSUPPORTED;
+  RouteOneOut ro;
+  ro.E = (int)E;
+  ro.K = top_k;
+  ro.topk_ids = topk_ids;
+  ro.topk_w = topk_w;
+  ro.offsets = expert_offsets;
+  ro.sorted = sorted_slots;
+  ro.rows = slot_rows;
+  ro.gsizes = group_sizes;
+  ro.gids = group_expert_ids;
+  ro.ngroups = num_groups;
+  const hipError_t e = launch_ffn_one_token(
+      plan, logits, x, gate_up_packed, gate_up_absmax, down_packed, down_absmax,
+      absmax_dtype == GNF4_DTYPE_BF16, (int)E, top_k, (int)H, (int)I, h, y,
+      static_cast<int32_t*>(workspace), ro, (hipStream_t)stream);
+  return e == hipSuccess ? GNF4_OK : hip_fail(e);
+}
+
+int gnf4_moe_ffn_one_token_supported(int64_t E, int32_t top_k, int64_t H, int64_t I) {
+  if (E < 1 || top_k < 1 || top_k > E || E > 128 || top_k > 32 || H < kBlock ||
+      H % kBlock != 0 || I < kBlock || I % kBlock != 0)
+    return 0;
+  FfnPlan plan;
+  return plan_ffn(E, top_k, H, I, device_cu_count(), plan) ? 1 : 0;
+}
+
 gnf4_status gnf4_swiglu(const uint16_t* gate_up, int64_t M, int64_t I, uint16_t* h,
                         void* stream) {
   if (M < 0 || I <= 0) return GNF4_ERR_INVALID_ARG;

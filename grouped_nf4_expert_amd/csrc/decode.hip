@@ -308,6 +308,89 @@ __device__ __forceinline__ void dword_terms(uint32_t d, const float (&xw)[R][8],
   }
 }
 
+// One token routed in the launch, in every wavefront: returns the expert of
+// the j-th pick in expert order.  Entry s of lane l holds expert l + 64 s's
+// key, as the route/sort kernels build it (rank_token): the logit's
+// order-preserving key above the complemented expert id, so keys are
+// distinct, larger is better and the lower id wins a tie.  The wavefront
+// finds the K-th largest key bit by bit from the top (a radix select over
+// ballot counts: the largest t with at least K keys >= t); the picks are the
+// keys >= t, the same set rank_token's ranks < K give.  Only the bits that
+// differ between keys are searched: the 32 of the logit's key, then the low
+// 7 of the id part (ids below 128 share bits 7..31 of ~id).  `issued` runs
+// once the logit loads are issued and returns K and j (kernel arguments it
+// reads arrive while the loads are in flight).  With `write`, the wavefront
+// also writes the route/sort outputs.
+struct PickQuery {
+  int k, j;
+};
+template <int EPL, typename Issued>
+__device__ __forceinline__ int route_pick(const float* __restrict__ logits, int E, int lane,
+                                          bool write, const RouteOneOut& ro, Issued&& issued) {
+  float val[EPL];
+  uint64_t key[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const int e = lane + kWave * s;
+    val[s] = e < E ? logits[e] : 0.0f;
+  }
+  const PickQuery q = issued();
+  const int kpick = q.k, j = q.j;
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    const int e = lane + kWave * s;
+    key[s] = e < E ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
+                   : 0ull;
+  }
+  uint64_t t = 0;
+  auto try_bit = [&](int b) {
+    const uint64_t cand = t | (1ull << b);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[s] >= cand));
+    if (cnt >= kpick) t = cand;
+  };
+#pragma unroll
+  for (int b = 63; b >= 32; --b) try_bit(b);
+  t |= 0xffffff80ull;
+#pragma unroll
+  for (int b = 6; b >= 0; --b) try_bit(b);
+  uint64_t sel[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) sel[s] = __builtin_amdgcn_ballot_w64(key[s] >= t);
+  // the j-th pick in expert order (entry 0 of every lane, then entry 1)
+  int jj = j;
+  int expert = 0;
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    uint64_t m = sel[s];
+    const int c = __popcll(m);
+    if (jj >= 0 && jj < c) {  // uniform
+      for (int q = 0; q < jj; ++q) m &= m - 1;
+      expert = kWave * s + __ffsll((unsigned long long)m) - 1;
+    }
+    jj -= c;
+  }
+  if (write) {
+    // the route/sort outputs need each pick's rank: the picks above it
+    int rank[EPL];
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) rank[s] = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < EPL; ++s2)
+      for (uint64_t m = sel[s2]; m; m &= m - 1) {
+        const uint64_t kj = readlane64(key[s2], __ffsll((unsigned long long)m) - 1);
+#pragma unroll
+        for (int s = 0; s < EPL; ++s) rank[s] += kj > key[s] ? 1 : 0;
+      }
+#pragma unroll
+    for (int s = 0; s < EPL; ++s)
+      if (!((sel[s] >> lane) & 1)) rank[s] = kpick;
+    route_one_token_write<EPL>(ro, lane, val, rank);
+  }
+  return expert;
+}
+
 // One group, one K split, a tile of weight rows; activation rows in chunks
 // of R (the weights stay in registers across chunks).
 //
@@ -343,84 +426,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   int my_slot = 0;
   GroupRef gr;
   if constexpr (ROUTED > 0) {
-    // One token routed in the launch.  Entry s of lane l holds expert
-    // l + 64 s's key, as the route/sort kernels build it (rank_token): the
-    // logit's order-preserving key above the complemented expert id, so keys
-    // are distinct, larger is better and the lower id wins a tie.  Every
-    // wavefront finds the K-th largest key on its own, bit by bit from the
-    // top (a radix select over ballot counts: the largest t with at least K
-    // keys >= t); the picks are the keys >= t, the same set rank_token's
-    // ranks < K give.  Only the bits that differ between keys are searched:
-    // the 32 of the logit's key, then the low 7 of the id part (ids below
-    // 128 share bits 7..31 of ~id).  Group j is the j-th pick in expert order,
-    // one row (row j, token 0).
-    constexpr int EPL = ROUTED;
-    const int E = k_E;
-    float val[EPL];
-    uint64_t key[EPL];
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) {
-      const int e = lane + kWave * s;
-      val[s] = e < E ? k_logits[e] : 0.0f;
-    }
-    pin_args(a);
-    const int kpick = a.route_k;
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) {
-      const int e = lane + kWave * s;
-      key[s] = e < E ? (((uint64_t)float_key(val[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e))
-                     : 0ull;
-    }
-    uint64_t t = 0;
-    auto try_bit = [&](int b) {
-      const uint64_t cand = t | (1ull << b);
-      int cnt = 0;
-#pragma unroll
-      for (int s = 0; s < EPL; ++s) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[s] >= cand));
-      if (cnt >= kpick) t = cand;
-    };
-#pragma unroll
-    for (int b = 63; b >= 32; --b) try_bit(b);
-    t |= 0xffffff80ull;
-#pragma unroll
-    for (int b = 6; b >= 0; --b) try_bit(b);
-    uint64_t sel[EPL];
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) sel[s] = __builtin_amdgcn_ballot_w64(key[s] >= t);
-    // the j-th pick in expert order (entry 0 of every lane, then entry 1)
     const int j = blockIdx.y;
-    int jj = j;
-    gr.expert = 0;
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) {
-      uint64_t m = sel[s];
-      const int c = __popcll(m);
-      if (jj >= 0 && jj < c) {  // uniform
-        for (int q = 0; q < jj; ++q) m &= m - 1;
-        gr.expert = kWave * s + __ffsll((unsigned long long)m) - 1;
-      }
-      jj -= c;
-    }
+    gr.expert = route_pick<ROUTED>(
+        k_logits, k_E, lane, blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0,
+        a.ro, [&]() {
+          pin_args(a);
+          return PickQuery{a.route_k, j};
+        });
     gr.g = j;
     gr.size = 1;
     gr.row = j;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0) {
-      // the route/sort outputs need each pick's rank: the picks above it
-      int rank[EPL];
-#pragma unroll
-      for (int s = 0; s < EPL; ++s) rank[s] = 0;
-#pragma unroll
-      for (int s2 = 0; s2 < EPL; ++s2)
-        for (uint64_t m = sel[s2]; m; m &= m - 1) {
-          const uint64_t kj = readlane64(key[s2], __ffsll((unsigned long long)m) - 1);
-#pragma unroll
-          for (int s = 0; s < EPL; ++s) rank[s] += kj > key[s] ? 1 : 0;
-        }
-#pragma unroll
-      for (int s = 0; s < EPL; ++s)
-        if (!((sel[s] >> lane) & 1)) rank[s] = kpick;
-      route_one_token_write<EPL>(a.ro, lane, val, rank);
-    }
   } else {
     if (slots_in_lanes && lane < k_M) my_slot = k_slots[lane];
     GroupChunk first;
@@ -687,6 +702,266 @@ int pick_lanes(int cps) {
   return best;
 }
 
+// ---------------------------------------------------------------------------
+// One token's MoE expert feed-forward in one launch (batch-1 decode):
+// routing, gate_up = x . W1[e]^T for each pick, h = silu(gate) * up, and
+// y = h . W2[e]^T, with no launch between the two projections.
+//
+// The grid holds K * gu_tiles gate_up workgroups, then K * dn_tiles down
+// workgroups (pick-major in both).  A gate_up workgroup computes P rows of the
+// gate half and the same P rows of the up half of its pick's W1 (2P weight
+// rows), finishes h for those P columns and counts itself done for the pick
+// (done(j)); the pick's last one raises its ready flags.  A down workgroup
+// issues its weight loads as soon as it knows its expert, then waits for its
+// pick's ready flag, reads h[j] and finishes.  Workgroups are dispatched in
+// grid order, so every gate_up workgroup is running or done before any down
+// workgroup starts waiting, and the gate_up workgroups wait on nothing: the
+// waits end.  A wait is bounded all the same (kFfnSpinLimit polls); one that
+// runs out sets the error word and goes on.  The last down workgroup of a
+// pick to pass the wait clears the pick's words for the next call.
+//
+// h and the words are written and read with device-scope atomic accesses,
+// which are performed where every XCD sees them, and a tile is counted only
+// after its h stores are complete: the ordering needs no cache write-back or
+// invalidation (those, one per workgroup, cost more than the launch saved).
+
+struct FfnKArgs {
+  // every wavefront reads these before its weight loads: 84 bytes
+  const uint8_t* gu_packed;
+  const void* gu_absmax;
+  const uint8_t* dn_packed;
+  const void* dn_absmax;
+  uint16_t* h;      // [K, I] bf16 bits
+  uint16_t* y;      // [K, H] bf16 bits
+  int32_t* sync;    // the counters and flags below, one per 128-byte line
+  int H, I, route_k;
+  int gu_tiles, dn_tiles;
+  int gu_rows, dn_rows;  // weight rows per workgroup
+  RouteOneOut ro;   // written by wavefront 0 of workgroup 0
+};
+
+constexpr int kFfnSpinLimit = 1 << 22;
+// Synchronisation words of the fused launch, each on a 128-byte line of its
+// own (index in int32 units; K picks):
+//   done(j)      gate_up workgroups of pick j finished
+//   passed(j)    down workgroups of pick j past their wait
+//   ready(j, x)  pick j's h complete, one flag per XCD x (its workgroups poll
+//                only their own XCD's line)
+//   error        set when a wait ran out
+constexpr int kSyncLine = 32;
+constexpr int kXcds = 8;
+__host__ __device__ constexpr int sync_done(int j) { return j * kSyncLine; }
+__host__ __device__ constexpr int sync_passed(int K, int j) { return (K + j) * kSyncLine; }
+__host__ __device__ constexpr int sync_ready(int K, int j, int x) {
+  return (2 * K + j * kXcds + x) * kSyncLine;
+}
+__host__ __device__ constexpr int sync_error(int K) { return (2 * K + K * kXcds) * kSyncLine; }
+
+__device__ __forceinline__ int xcd_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & (kXcds - 1));
+}
+
+__device__ __forceinline__ void pin_ffn_args(const FfnKArgs& a) {
+  asm volatile("" ::"s"(a.gu_packed), "s"(a.gu_absmax), "s"(a.dn_packed), "s"(a.dn_absmax),
+               "s"(a.h), "s"(a.y), "s"(a.sync), "s"(a.H), "s"(a.I), "s"(a.route_k),
+               "s"(a.gu_tiles), "s"(a.dn_tiles), "s"(a.gu_rows), "s"(a.dn_rows)
+               : "memory");
+}
+
+__device__ __forceinline__ float ffn_silu(float g) { return g / (1.0f + expf(-g)); }
+
+// The lane's NU weight rows (consecutive from n_base) against one activation
+// row staged in LDS (XStage layout, plane = chunks + 1): team-summed results,
+// valid in the team's last lane.
+template <int L, int NU, int STEPS, typename AbsT>
+__device__ __forceinline__ void ffn_rows(const float4* s_x, int plane, const float* lut, int tl,
+                                         int cpr, const uint4 (&wq)[STEPS][NU],
+                                         const float (&av)[STEPS][NU], float (&acc)[NU]) {
+#pragma unroll
+  for (int j = 0; j < NU; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int c = tl + st * L;
+    if (c >= cpr) continue;
+    float pr[NU][1];
+#pragma unroll
+    for (int j = 0; j < NU; ++j) pr[j][0] = 0.0f;
+    float xw[4][1][8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4* src = s_x + (2 * w) * plane + c;
+      const float4 lo = src[0], hi = src[plane];
+      xw[w][0][0] = lo.x; xw[w][0][1] = lo.y; xw[w][0][2] = lo.z; xw[w][0][3] = lo.w;
+      xw[w][0][4] = hi.x; xw[w][0][5] = hi.y; xw[w][0][6] = hi.z; xw[w][0][7] = hi.w;
+    }
+#pragma unroll
+    for (int j = 0; j < NU; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t d = w == 0 ? wq[st][j].x : w == 1 ? wq[st][j].y : w == 2 ? wq[st][j].z : wq[st][j].w;
+        asm volatile("" : "+v"(d));  // decode row j as soon as its load is in
+        dword_terms<1, AbsT>(d, xw[w], lut, pr[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < NU; ++j) acc[j] = fmaf(av[st][j], pr[j][0], acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NU; ++j) acc[j] = team_sum<L>(acc[j]);
+}
+
+template <int LG, int NUG, int STG, int LD, int NUD, int STD, typename AbsT, int EPL>
+__global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__ k_logits,
+                                                       const uint16_t* __restrict__ k_x, int k_E,
+                                                       FfnKArgs a) {
+  __shared__ float s_lut[32];
+  __shared__ float s_sum[kThreads];
+  extern __shared__ float4 s_x[];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wg = blockIdx.x;
+  // (1) route (every wavefront; the arguments arrive while the logits load)
+  bool gate_up = false;
+  int j = 0, t = 0;
+  const int expert = route_pick<EPL>(k_logits, k_E, lane, wg == 0 && wave == 0, a.ro, [&]() {
+    pin_ffn_args(a);
+    const int n_gu = a.route_k * a.gu_tiles;
+    gate_up = wg < n_gu;
+    const int local = gate_up ? wg : wg - n_gu;
+    const int tiles = gate_up ? a.gu_tiles : a.dn_tiles;
+    j = local / tiles;
+    t = local - j * tiles;
+    return PickQuery{a.route_k, j};
+  });
+  if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
+  const float* lut = s_lut;
+  const int H = a.H, I = a.I, K = a.route_k;
+
+  if (gate_up) {
+    // (2) gate_up: weight rows {t P + r} of the gate half and {I + t P + r} of
+    // the up half, r < P; K = H
+    constexpr int RPW = kWave / LG;
+    const int team = lane / LG, tl = lane % LG;
+    const int P = a.gu_rows / 2;
+    const int r0 = wave * (RPW * NUG) + team * NUG;  // a lane's rows stay in one half
+    const int n_base = r0 < P ? t * P + r0 : I + t * P + (r0 - P);
+    const int cpr = H / 32, bpr = H / kBlock;
+    const uint8_t* wexp = a.gu_packed + (size_t)expert * (2 * I) * (H / 2);
+    const AbsT* aexp = static_cast<const AbsT*>(a.gu_absmax) + (size_t)expert * (2 * I) * bpr;
+    XStage<1, x_batch(1, LG, STG)> stage;
+    stage.init(0, cpr);
+    const int xrow[1] = {0};
+    stage.load(k_x, H, xrow, 0);
+    uint4 wq[STG][NUG];
+    float av[STG][NUG];
+#pragma unroll
+    for (int st = 0; st < STG; ++st) {
+      const int c = tl + st * LG;
+      load_weights<NUG, AbsT>(wexp, aexp, (size_t)H / 2, bpr, 2 * I, n_base, c, c < cpr, wq[st],
+                              av[st]);
+    }
+    stage.store(s_x, 0);
+    lds_barrier();
+    float acc[NUG];
+    ffn_rows<LG, NUG, STG, AbsT>(s_x, stage.plane, lut, tl, cpr, wq, av, acc);
+    if (tl == LG - 1) {
+#pragma unroll
+      for (int jj = 0; jj < NUG; ++jj) s_sum[r0 + jj] = acc[jj];
+    }
+    __syncthreads();
+    // h for the P columns, two per 32-bit word, stored at device scope (the
+    // down workgroups read them from other XCDs)
+    if ((int)threadIdx.x < P / 2) {
+      const int i0 = 2 * threadIdx.x;
+      const uint32_t lo = f32_to_bf16(ffn_silu(s_sum[i0]) * s_sum[P + i0]);
+      const uint32_t hi = f32_to_bf16(ffn_silu(s_sum[i0 + 1]) * s_sum[P + i0 + 1]);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(a.h + (size_t)j * I + t * P) + threadIdx.x,
+                         lo | (hi << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Count this tile done once its stores are complete (P <= 128: the
+    // storing threads are wavefront 0's, which waits for them here, before
+    // thread 0's count); the pick's last tile raises the ready flags, after
+    // the count that shows every other tile's stores complete.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int prev = __hip_atomic_fetch_add(a.sync + sync_done(j), 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == a.gu_tiles - 1)
+        for (int x = 0; x < kXcds; ++x)
+          __hip_atomic_store(a.sync + sync_ready(K, j, x), 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  // (3) down: weight rows t * dn_rows + ..; K = I.  The weight loads go out
+  // first, then the wait for the pick's h.
+  constexpr int RPW = kWave / LD;
+  const int team = lane / LD, tl = lane % LD;
+  const int n_base = t * a.dn_rows + wave * (RPW * NUD) + team * NUD;
+  const int cpr = I / 32, bpr = I / kBlock;
+  const uint8_t* wexp = a.dn_packed + (size_t)expert * H * (I / 2);
+  const AbsT* aexp = static_cast<const AbsT*>(a.dn_absmax) + (size_t)expert * H * bpr;
+  uint4 wq[STD][NUD];
+  float av[STD][NUD];
+#pragma unroll
+  for (int st = 0; st < STD; ++st) {
+    const int c = tl + st * LD;
+    load_weights<NUD, AbsT>(wexp, aexp, (size_t)I / 2, bpr, H, n_base, c, c < cpr, wq[st], av[st]);
+  }
+  // One poller per workgroup, on its XCD's ready line, about every 0.25 us
+  // (the first poll returns after the weight loads: loads complete in order).
+  if (threadIdx.x == 0) {
+    const int* flag = a.sync + sync_ready(K, j, xcd_id());
+    int spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      if (++spins > kFfnSpinLimit) {
+        __hip_atomic_store(a.sync + sync_error(K), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    // the pick's last down workgroup past the wait re-arms its words
+    const int passed = __hip_atomic_fetch_add(a.sync + sync_passed(K, j), 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (passed == a.dn_tiles - 1) {
+      __hip_atomic_store(a.sync + sync_done(j), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.sync + sync_passed(K, j), 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < kXcds; ++x)
+        __hip_atomic_store(a.sync + sync_ready(K, j, x), 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  // h row j at device scope, 32-bit words -> fp32 in the staging layout
+  // (32 values per chunk c: piece p = 4 values at slot p * plane + c)
+  XStage<1, x_batch(1, LD, STD)> stage;
+  stage.init(0, cpr);
+  {
+    const uint32_t* hw = reinterpret_cast<const uint32_t*>(a.h + (size_t)j * I);
+    for (int q = threadIdx.x; q < I / 2; q += kThreads) {
+      const uint32_t v = __hip_atomic_load(hw + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int e0 = 2 * q;
+      const int c = e0 / 32, within = e0 % 32;
+      float* dst = reinterpret_cast<float*>(s_x + (within / 4) * stage.plane + c) + within % 4;
+      dst[0] = __uint_as_float(v << 16);
+      dst[1] = __uint_as_float(v & 0xffff0000u);
+    }
+  }
+  lds_barrier();
+  float acc[NUD];
+  ffn_rows<LD, NUD, STD, AbsT>(s_x, stage.plane, lut, tl, cpr, wq, av, acc);
+  if (tl == LD - 1) {
+#pragma unroll
+    for (int jj = 0; jj < NUD; ++jj) {
+      const int n = n_base + jj;
+      if (n < H) a.y[(size_t)j * H + n] = f32_to_bf16(acc[jj]);
+    }
+  }
+}
+
 }  // namespace
 
 // Launch rule (host-known sizes only).  Rows per pass R from the rows per
@@ -835,6 +1110,127 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
   }
   if (err != hipSuccess || p.S == 1) return err;
   return launch_reduce(a, stream);
+}
+
+// ------------------------------------------------------------ fused FFN
+// The FFN launch's two roles take the plans the one-token decode launches
+// would (no K split); the kernel is instantiated for the role pairs below.
+bool plan_ffn(int64_t E, int top_k, int64_t H, int64_t I, int num_cus, FfnPlan& out) {
+  (void)E;
+  out.gu = plan_decode(top_k, 2 * I, H, top_k, 1, num_cus);
+  out.dn = plan_decode(top_k, H, I, top_k, 1, num_cus);
+  const DecodePlan& g = out.gu;
+  const DecodePlan& d = out.dn;
+  if (g.L == 0 || d.L == 0 || g.S != 1 || d.S != 1 || g.R != 1 || d.R != 1) return false;
+  if (g.rows_per_block % 2 != 0 || I % (g.rows_per_block / 2) != 0) return false;
+  if (g.rows_per_block > kThreads) return false;
+  if (g.cps + 1 > kXSlots || d.cps + 1 > kXSlots) return false;
+  out.gu_tiles = (int)(I / (g.rows_per_block / 2));
+  out.dn_tiles = d.n_tiles;
+  if (!ffn_supported(out)) return false;
+  // Every workgroup resident at once: the down workgroups then load their
+  // weights while gate_up runs (the point of the fused launch), and no
+  // waiting workgroup can hold a slot a gate_up workgroup needs.
+  const int64_t grid = (int64_t)top_k * (out.gu_tiles + out.dn_tiles);
+  return grid <= (int64_t)ffn_resident_per_cu(out, E > kWave) * num_cus;
+}
+
+namespace {
+
+// role plans (L, NU, steps) the kernel is built for, as pairs
+#define GNF4_FFN_PAIRS(X)                  \
+  X(64, 4, 1, 32, 2, 1) /* OLMoE   */     \
+  X(64, 2, 1, 8, 1, 3)  /* Qwen3   */     \
+  X(32, 1, 3, 32, 1, 3) /* GPT-OSS */
+
+template <int LG, int NUG, int STG, int LD, int NUD, int STD, typename AbsT, int EPL>
+hipError_t launch_ffn_one(const float* logits, const uint16_t* x, int E, const FfnKArgs& a,
+                          int grid, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((ffn_kernel<LG, NUG, STG, LD, NUD, STD, AbsT, EPL>), dim3(grid),
+                     dim3(kThreads), lds, stream, logits, x, E, a);
+  return hipGetLastError();
+}
+
+bool pair_is(const FfnPlan& p, int lg, int nug, int stg, int ld, int nud, int std_) {
+  return p.gu.L == lg && p.gu.NU == nug && p.gu.steps == stg && p.dn.L == ld &&
+         p.dn.NU == nud && p.dn.steps == std_;
+}
+
+}  // namespace
+
+// Workgroups of the fused kernel one CU holds at once (the occupancy query
+// on the current device; without one, 8: 256-thread workgroups of at most
+// 64 VGPRs and the kernel's LDS).
+int ffn_resident_per_cu(const FfnPlan& p, bool two_entries) {
+  const size_t lds = (size_t)(p.gu.cps > p.dn.cps ? p.gu.cps + 1 : p.dn.cps + 1) * 128;
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+#define GNF4_FFN_OCC(lg, nug, stg, ld, nud, std_)                                                  \
+  if (pair_is(p, lg, nug, stg, ld, nud, std_))                                                     \
+    e = two_entries ? hipOccupancyMaxActiveBlocksPerMultiprocessor(                                \
+                          &n, ffn_kernel<lg, nug, stg, ld, nud, std_, float, 2>, kThreads, lds)    \
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(                                \
+                          &n, ffn_kernel<lg, nug, stg, ld, nud, std_, float, 1>, kThreads, lds);
+  GNF4_FFN_PAIRS(GNF4_FFN_OCC)
+#undef GNF4_FFN_OCC
+  if (e != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 8;
+  }
+  return n;
+}
+
+size_t ffn_sync_bytes(int top_k) {
+  return (size_t)(sync_error(top_k) + kSyncLine) * sizeof(int32_t);
+}
+
+bool ffn_supported(const FfnPlan& p) {
+#define GNF4_FFN_MATCH(lg, nug, stg, ld, nud, std_) \
+  if (pair_is(p, lg, nug, stg, ld, nud, std_)) return true;
+  GNF4_FFN_PAIRS(GNF4_FFN_MATCH)
+#undef GNF4_FFN_MATCH
+  return false;
+}
+
+hipError_t launch_ffn_one_token(const FfnPlan& p, const float* logits, const uint16_t* x,
+                                const uint8_t* gu_packed, const void* gu_absmax,
+                                const uint8_t* dn_packed, const void* dn_absmax, bool abs_bf16,
+                                int E, int top_k, int H, int I, uint16_t* h, uint16_t* y,
+                                int32_t* sync, const RouteOneOut& ro, hipStream_t stream) {
+  FfnKArgs a;
+  a.gu_packed = gu_packed;
+  a.gu_absmax = gu_absmax;
+  a.dn_packed = dn_packed;
+  a.dn_absmax = dn_absmax;
+  a.h = h;
+  a.y = y;
+  a.sync = sync;
+  a.H = H;
+  a.I = I;
+  a.route_k = top_k;
+  a.gu_tiles = p.gu_tiles;
+  a.dn_tiles = p.dn_tiles;
+  a.gu_rows = p.gu.rows_per_block;
+  a.dn_rows = p.dn.rows_per_block;
+  a.ro = ro;
+  const int grid = top_k * (p.gu_tiles + p.dn_tiles);
+  const size_t lds = (size_t)(p.gu.cps > p.dn.cps ? p.gu.cps + 1 : p.dn.cps + 1) * 128;
+  const bool two = E > kWave;
+#define GNF4_FFN_LAUNCH(lg, nug, stg, ld, nud, std_)                                              \
+  if (pair_is(p, lg, nug, stg, ld, nud, std_)) {                                                  \
+    if (abs_bf16)                                                                                 \
+      return two ? launch_ffn_one<lg, nug, stg, ld, nud, std_, uint16_t, 2>(logits, x, E, a, grid, \
+                                                                            lds, stream)          \
+                 : launch_ffn_one<lg, nug, stg, ld, nud, std_, uint16_t, 1>(logits, x, E, a, grid, \
+                                                                            lds, stream);         \
+    return two ? launch_ffn_one<lg, nug, stg, ld, nud, std_, float, 2>(logits, x, E, a, grid, lds, \
+                                                                       stream)                    \
+               : launch_ffn_one<lg, nug, stg, ld, nud, std_, float, 1>(logits, x, E, a, grid, lds, \
+                                                                       stream);                   \
+  }
+  GNF4_FFN_PAIRS(GNF4_FFN_LAUNCH)
+#undef GNF4_FFN_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gnf4

@@ -131,4 +131,24 @@ __device__ void route_one_token_write(const RouteOneOut& o, int lane, const floa
 hipError_t launch_decode_routed(const GemmArgs& g, const DecodePlan& p, const float* logits,
                                 const RouteOneOut& ro, hipStream_t stream);
 
+// One token's expert feed-forward in one launch (decode.hip): routing,
+// gate_up [E, 2I, H] (gate half first), SwiGLU, down [E, H, I].  The two
+// projections use the plans their one-token decode launches would, unsplit.
+struct FfnPlan {
+  DecodePlan gu, dn;
+  int gu_tiles, dn_tiles;  // workgroups per pick
+};
+bool ffn_supported(const FfnPlan& p);
+int ffn_resident_per_cu(const FfnPlan& p, bool two_entries);
+// bytes of the launch's synchronisation words for top_k picks
+size_t ffn_sync_bytes(int top_k);
+// false when the shapes have no fused kernel (the caller then runs the steps
+// as separate launches)
+bool plan_ffn(int64_t E, int top_k, int64_t H, int64_t I, int num_cus, FfnPlan& out);
+hipError_t launch_ffn_one_token(const FfnPlan& p, const float* logits, const uint16_t* x,
+                                const uint8_t* gu_packed, const void* gu_absmax,
+                                const uint8_t* dn_packed, const void* dn_absmax, bool abs_bf16,
+                                int E, int top_k, int H, int I, uint16_t* h, uint16_t* y,
+                                int32_t* sync, const RouteOneOut& ro, hipStream_t stream);
+
 }  // namespace gnf4

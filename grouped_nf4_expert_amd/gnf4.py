@@ -82,6 +82,13 @@ def library():
                                             i64, vp, vp, sz, i32, i32, vp]
     lib.gnf4_swiglu.restype = ctypes.c_int
     lib.gnf4_swiglu.argtypes = [vp, i64, i64, vp, vp]
+    lib.gnf4_moe_ffn_one_token_workspace_size.restype = sz
+    lib.gnf4_moe_ffn_one_token_workspace_size.argtypes = [i32]
+    lib.gnf4_moe_ffn_one_token_supported.restype = ctypes.c_int
+    lib.gnf4_moe_ffn_one_token_supported.argtypes = [i64, i32, i64, i64]
+    lib.gnf4_moe_ffn_one_token.restype = ctypes.c_int
+    lib.gnf4_moe_ffn_one_token.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, i32, i64, i64, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gnf4_combine.restype = ctypes.c_int
     lib.gnf4_combine.argtypes = [vp, vp, vp, i64, i32, i64, i64, vp, vp]
     lib.gnf4_gather_rows.restype = ctypes.c_int
@@ -250,6 +257,64 @@ def route_gemm_one_token(logits, x, packed, absmax, top_k, buffers=None, y=None,
         _ptr(r.slot_rows), _ptr(r.group_sizes), _ptr(r.group_expert_ids), _ptr(r.num_groups),
         _ptr(workspace), ws_bytes, _stream()), "gnf4_route_gemm_one_token")
     return y, r
+
+
+def moe_ffn_one_token_workspace(top_k, device):
+    """The per-pick counters of moe_ffn_one_token, zeroed (every call leaves
+    them zero again); the last int32 is the error flag."""
+    n = library().gnf4_moe_ffn_one_token_workspace_size(top_k)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_ffn_one_token_supported(E, top_k, H, I):
+    return bool(library().gnf4_moe_ffn_one_token_supported(E, top_k, H, I))
+
+
+def moe_ffn_one_token(logits, x, gate_up, down, top_k, buffers=None, h=None, y=None,
+                      workspace=None):
+    """One token's MoE expert feed-forward in one launch: route/sort,
+    gate_up over the picks, SwiGLU, down.  ``logits`` [1, E] fp32 (E <= 128),
+    ``x`` [1, H] bf16, ``gate_up`` = (packed [E, 2I, H/2], absmax) with the
+    gate rows first, ``down`` = (packed [E, H, I/2], absmax).  Returns
+    (y [top_k, H], h [top_k, I], RouteResult), rows in grouped order; the
+    weighted combine is combine(y, ...).  ``workspace`` (from
+    moe_ffn_one_token_workspace) may be reused across calls on one stream."""
+    _need(logits, "logits", torch.float32, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    gp, ga = gate_up
+    dp, da = down
+    for t, n in ((gp, "gate_up packed"), (dp, "down packed")):
+        _need(t, n, torch.uint8, 3)
+    for t, n in ((ga, "gate_up absmax"), (da, "down absmax")):
+        _need(t, n, t.dtype, 3)
+    adt = _absmax_dtype(ga)
+    if _absmax_dtype(da) != adt:
+        raise ValueError("gate_up and down absmax dtypes differ")
+    T, E = logits.shape
+    if T != 1 or x.shape[0] != 1:
+        raise ValueError("moe_ffn_one_token routes exactly one token")
+    H = x.shape[1]
+    if gp.shape[0] != E or gp.shape[2] * 2 != H or gp.shape[1] % 2 != 0:
+        raise ValueError("gate_up stack must be [E, 2I, H/2]")
+    I = gp.shape[1] // 2
+    if dp.shape != (E, H, I // 2) or ga.shape != (E, 2 * I, H // 64) or da.shape != (E, H, I // 64):
+        raise ValueError("down stack must be [E, H, I/2] with absmax [E, H, I/64]")
+    if buffers is None:
+        buffers = RouteBuffers(1, E, top_k, logits.device)
+    r = buffers.result
+    if h is None:
+        h = torch.empty((top_k, I), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((top_k, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = moe_ffn_one_token_workspace(top_k, x.device)
+    _check(library().gnf4_moe_ffn_one_token(
+        _ptr(logits), E, top_k, _ptr(x), _ptr(gp), _ptr(ga), _ptr(dp), _ptr(da), adt, H, I,
+        _ptr(h), _ptr(y), _ptr(r.topk_ids), _ptr(r.topk_w), _ptr(r.expert_offsets),
+        _ptr(r.sorted_slots), _ptr(r.slot_rows), _ptr(r.group_sizes), _ptr(r.group_expert_ids),
+        _ptr(r.num_groups), _ptr(workspace), workspace.numel(), _stream()),
+        "gnf4_moe_ffn_one_token")
+    return y, h, r
 
 
 # ------------------------------------------------------------------ MXFP4

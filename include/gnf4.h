@@ -203,6 +203,68 @@ gnf4_status gnf4_route_gemm_one_token(const float* logits, int64_t E, int32_t to
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gnf4_moe_ffn_one_token -- one token's MoE expert feed-forward in one
+ * launch: the route/sort of gnf4_route_gemm_one_token, then for each pick
+ * e_j (ascending expert id, j < top_k)
+ *   g = x . W1[e_j]^T          (W1: [E, 2I, H], gate rows 0..I-1, up rows I..2I-1)
+ *   h[j, i] = bf16(silu(g[i]) * g[I + i]),  silu(v) = v / (1 + exp(-v))
+ *   y[j, :] = bf16(h[j, :] . W2[e_j]^T)  (W2: [E, H, I])
+ * with fp32 accumulation and the SwiGLU taken on the fp32 sums.
+ *
+ * Landing page "grouped-nf4-gemm": "Owns" (the grouped GEMM and the decode
+ * glue kernels, SwiGLU among them) and "Use this when" (a decode step's small
+ * operations in as few launches as possible); the projections as
+ * gnf4_route_gemm_one_token and gnf4_grouped_gemm, the activation as
+ * gnf4_swiglu.  The weighted combine stays a separate call (gnf4_combine
+ * with y and slot_rows).  The down workgroups load their weights while the
+ * gate_up workgroups run and wait, per pick, for that pick's h: no launch
+ * separates the two projections.
+ *
+ *   logits            [E] fp32 router logits of the token (finite)
+ *   x                 [H] bf16 bits, 16-byte aligned
+ *   gate_up_packed, gate_up_absmax   [E, 2I, H/2] uint8, [E, 2I, H/64] absmax
+ *   down_packed, down_absmax         [E, H, I/2] uint8, [E, H, I/64] absmax
+ *                     (`absmax_dtype` for both; packed 16-byte aligned)
+ *   h                 [top_k, I] bf16 bits out (16-byte aligned): row j the
+ *                     SwiGLU of pick j
+ *   y                 [top_k, H] bf16 bits out: row j the down projection of
+ *                     pick j (the grouped order gnf4_combine reads)
+ *   topk_ids ... num_groups: as gnf4_route_sort for T = 1 (slot_rows optional)
+ *   workspace         device memory of gnf4_moe_ffn_one_token_workspace_size()
+ *                     bytes (4-byte aligned): per-pick counters and flags that
+ *                     MUST be zero before the first call (hipMemset once);
+ *                     every call that completes normally leaves all of it zero
+ *                     again, so one workspace serves any number of calls on
+ *                     one stream.  Calls sharing a workspace must not overlap.
+ *                     A nonzero word after a call means a wait ran out (an
+ *                     error word is set and never cleared): that call's
+ *                     outputs are not to be trusted.
+ *
+ * Limits: as gnf4_route_gemm_one_token (E <= 128, top_k <= min(E, 32)),
+ * H % 64 == 0, I % 64 == 0; the fused kernel exists for the role shapes of
+ * the OLMoE and Qwen3-30B expert layers, and only where all of its
+ * workgroups fit on the device at once (GPT-OSS-120B's do not).
+ * gnf4_moe_ffn_one_token_supported() says whether a shape is served;
+ * otherwise GNF4_ERR_UNSUPPORTED, and the three steps run as separate calls.
+ * Tolerance and determinism as gnf4_grouped_gemm for each projection.
+ * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_UNSUPPORTED,
+ * GNF4_ERR_WORKSPACE, GNF4_ERR_HIP.
+ */
+size_t gnf4_moe_ffn_one_token_workspace_size(int32_t top_k);
+
+int gnf4_moe_ffn_one_token_supported(int64_t E, int32_t top_k, int64_t H, int64_t I);
+
+gnf4_status gnf4_moe_ffn_one_token(const float* logits, int64_t E, int32_t top_k,
+                                   const uint16_t* x, const uint8_t* gate_up_packed,
+                                   const void* gate_up_absmax, const uint8_t* down_packed,
+                                   const void* down_absmax, int32_t absmax_dtype, int64_t H,
+                                   int64_t I, uint16_t* h, uint16_t* y, int32_t* topk_ids,
+                                   float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                                   int32_t* slot_rows, int32_t* group_sizes,
+                                   int32_t* group_expert_ids, int32_t* num_groups,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gnf4_gather_rows -- build the grouped activations from token rows:
  * x_sorted[r, :] = x[sorted_slots[r] / top_k, :] for r < M.
  *

@@ -210,3 +210,40 @@ def test_noalloc_rejects_bad_arguments(lib):
     big[7], big[8], big[11], big[12], big[14] = 4096, 7168, 256, 32768, 2
     assert f(*big) == 3
 
+
+
+def test_moe_ffn_one_token_rejects_bad_arguments(lib):
+    lib.gnf4_moe_ffn_one_token_workspace_size.restype = ctypes.c_size_t
+    lib.gnf4_moe_ffn_one_token_workspace_size.argtypes = [ctypes.c_int32]
+    # 10 k + 1 words, one per 128-byte line
+    assert lib.gnf4_moe_ffn_one_token_workspace_size(8) == 81 * 128
+    assert lib.gnf4_moe_ffn_one_token_workspace_size(0) == 0
+    sup = lib.gnf4_moe_ffn_one_token_supported
+    sup.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
+    assert sup(64, 8, 2048, 1024) == 1          # OLMoE expert layer
+    assert sup(128, 8, 2048, 768) == 1          # Qwen3-30B
+    assert sup(128, 4, 2880, 2880) == 0         # GPT-OSS-120B: more workgroups than fit at once
+    assert sup(8, 2, 256, 128) == 0             # no fused kernel for this shape
+    assert sup(200, 8, 2048, 1024) == 0         # more experts than the routing handles
+    f = lib.gnf4_moe_ffn_one_token
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    f.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                  vp, vp, vp, sz, vp]
+    # logits, E, k, x, gp, ga, dp, da, dtype, H, I, h, y, 8 route outputs, ws, ws_bytes, stream
+    ok = [FAKE, 64, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2048, 1024, FAKE, FAKE] + [FAKE] * 8 + \
+         [FAKE, 81 * 128, NULL]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a1=0) == 1            # E
+    assert call(a2=65) == 1           # top_k > E
+    assert call(a9=2000) == 1         # H % 64
+    assert call(a10=96) == 1          # I % 64
+    assert call(a8=7) == 1            # absmax dtype
+    assert call(a3=NULL) == 1         # x
+    assert call(a1=200) == 3          # E > 128
+    assert call(a2=33, a1=64) == 3    # top_k > 32
+    assert call(a21=NULL) == 4        # no workspace
+    assert call(a22=80 * 128) == 4    # workspace too small
