@@ -73,7 +73,8 @@ struct DecodeKArgs {
   double inv_slot_div;  // 1 / slot_div, for the fused gather's row index
   int N, K, T, slot_div, rows_max_decode;
   int S, cps, cpr, rows_per_block;
-  int route_k;  // picks per token of the routed launch (ro.K)
+  int16_t route_k;  // picks per token of the routed launch (ro.K)
+  int16_t vec_out;  // S == 1, R == 1, N % NU == 0, y aligned: one NU-wide store per lane
   // the rest: the split-K reduce's arguments and the route/sort outputs,
   // which only workgroup (0, 0, 0) of the routed launch writes
   GemmArgs g;
@@ -154,21 +155,22 @@ __device__ __forceinline__ void e2m1_pair(uint32_t d, float& first, float& secon
 // been issued) before the activations staged ahead of them and before the
 // first row's decode.
 template <int NU, typename AbsT>
-__device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* aexp,
-                                             size_t row_bytes, int bpr, int N, int n_base, int c,
-                                             bool valid, uint4 (&wq)[NU], float (&av)[NU]) {
+__device__ __forceinline__ void load_weights(const uint8_t* wexp, const AbsT* aexp, int row_bytes,
+                                             int bpr, int N, int n_base, int c, bool valid,
+                                             uint4 (&wq)[NU], float (&av)[NU]) {
+  // offsets inside one expert fit 31 bits (N * K/2 < 2^31 is a call limit)
 #pragma unroll
   for (int j = 0; j < NU; ++j) {
     const int n = n_base + j;
     const bool ok = valid && n < N;
-    const size_t nn = ok ? (size_t)n : 0;
-    const size_t cc = ok ? (size_t)c : 0;
-    const uint4 q = *reinterpret_cast<const uint4*>(wexp + nn * row_bytes + 16 * cc);
+    const uint32_t nn = ok ? (uint32_t)n : 0u;
+    const uint32_t cc = ok ? (uint32_t)c : 0u;
+    const uint4 q = *reinterpret_cast<const uint4*>(wexp + (nn * (uint32_t)row_bytes + 16u * cc));
     float v;
     if constexpr (kMxfp4<AbsT>)
-      v = e8m0_to_f32(aexp[nn * (2 * bpr) + cc]);  // one scale per chunk
+      v = e8m0_to_f32(aexp[nn * (uint32_t)(2 * bpr) + cc]);  // one scale per chunk
     else
-      v = absmax_at(aexp, nn * bpr + (cc >> 1));
+      v = absmax_at(aexp, nn * (uint32_t)bpr + (cc >> 1));
     wq[j] = q;
     av[j] = v;
   }
@@ -261,7 +263,7 @@ __device__ __forceinline__ int div_slot(int n, int d, double inv_d) {
 __device__ __forceinline__ void pin_args(const DecodeKArgs& a) {
   asm volatile("" ::"s"(a.x), "s"(a.packed), "s"(a.absmax), "s"(a.out), "s"(a.inv_slot_div),
                "s"(a.N), "s"(a.K), "s"(a.T), "s"(a.slot_div), "s"(a.rows_max_decode), "s"(a.S),
-               "s"(a.cps), "s"(a.cpr), "s"(a.rows_per_block), "s"(a.route_k)
+               "s"(a.cps), "s"(a.cpr), "s"(a.rows_per_block), "s"(a.route_k), "s"(a.vec_out)
                : "memory");
 }
 
@@ -426,13 +428,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   int my_slot = 0;
   GroupRef gr;
   if constexpr (ROUTED > 0) {
+    // Up to 64 experts every wavefront routes for itself (no wait for a
+    // neighbour); with two router entries per lane the ranking is twice the
+    // work and wavefront 0 does it for the workgroup, the others reading its
+    // answer from LDS (measured: faster for 128 experts, slower for 64).
     const int j = blockIdx.y;
-    gr.expert = route_pick<ROUTED>(
-        k_logits, k_E, lane, blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0,
-        a.ro, [&]() {
-          pin_args(a);
-          return PickQuery{a.route_k, j};
-        });
+    const bool write = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0;
+    auto issued = [&]() {
+      pin_args(a);
+      return PickQuery{a.route_k, j};
+    };
+    if constexpr (ROUTED == 1) {
+      gr.expert = route_pick<ROUTED>(k_logits, k_E, lane, write, a.ro, issued);
+    } else {
+      __shared__ int s_expert;
+      if (wave == 0) {
+        const int e = route_pick<ROUTED>(k_logits, k_E, lane, write, a.ro, issued);
+        if (lane == 0) s_expert = e;
+      } else {
+        pin_args(a);
+      }
+      __syncthreads();
+      gr.expert = s_expert;
+    }
     gr.g = j;
     gr.size = 1;
     gr.row = j;
@@ -494,7 +512,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int c = c_begin + tl + st * L;
-    load_weights<NU, AbsT>(wexp, aexp, row_bytes, bpr, N, n_base, c, c < c_end, wq[st], av[st]);
+    load_weights<NU, AbsT>(wexp, aexp, (int)row_bytes, bpr, N, n_base, c, c < c_end, wq[st],
+                           av[st]);
   }
   stage.store(s_x, 0);
 
@@ -564,6 +583,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       for (int r = 0; r < R; ++r) acc[j][r] = team_sum<L>(acc[j][r]);
 
     // the team's last lane holds the sums
+    if constexpr (R == 1 && (NU == 2 || NU == 4)) {
+      if (a.vec_out && tl == L - 1 && xrow[0] >= 0 && n_base < N) {
+        // the lane's NU outputs are consecutive in row r0: one store
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        auto pk = [](float lo, float hi) {
+          return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+        };
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + (size_t)r0 * N + n_base;
+        if constexpr (NU == 4)
+          *reinterpret_cast<uint2*>(dst) =
+              make_uint2(pk(acc[0][0], acc[1][0]), pk(acc[2][0], acc[3][0]));
+        else
+          *reinterpret_cast<uint32_t*>(dst) = pk(acc[0][0], acc[1][0]);
+        return;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
       const int n = n_base + j;
@@ -811,8 +847,10 @@ __device__ __forceinline__ void ffn_rows(const float4* s_x, int plane, const flo
   for (int j = 0; j < NU; ++j) acc[j] = team_sum<L>(acc[j]);
 }
 
+// At most 64 VGPRs (eight wavefronts per SIMD): eight workgroups per CU, so
+// the OLMoE- and Qwen3-shaped launches fit on the device at once.
 template <int LG, int NUG, int STG, int LD, int NUD, int STD, typename AbsT, int EPL>
-__global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__ k_logits,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void ffn_kernel(const float* __restrict__ k_logits,
                                                        const uint16_t* __restrict__ k_x, int k_E,
                                                        FfnKArgs a) {
   __shared__ float s_lut[32];
@@ -823,7 +861,7 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__
   // (1) route (every wavefront; the arguments arrive while the logits load)
   bool gate_up = false;
   int j = 0, t = 0;
-  const int expert = route_pick<EPL>(k_logits, k_E, lane, wg == 0 && wave == 0, a.ro, [&]() {
+  auto place = [&]() {
     pin_ffn_args(a);
     const int n_gu = a.route_k * a.gu_tiles;
     gate_up = wg < n_gu;
@@ -832,7 +870,8 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__
     j = local / tiles;
     t = local - j * tiles;
     return PickQuery{a.route_k, j};
-  });
+  };
+  const int expert = route_pick<EPL>(k_logits, k_E, lane, wg == 0 && wave == 0, a.ro, place);
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const float* lut = s_lut;
   const int H = a.H, I = a.I, K = a.route_k;
@@ -857,7 +896,7 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__
 #pragma unroll
     for (int st = 0; st < STG; ++st) {
       const int c = tl + st * LG;
-      load_weights<NUG, AbsT>(wexp, aexp, (size_t)H / 2, bpr, 2 * I, n_base, c, c < cpr, wq[st],
+      load_weights<NUG, AbsT>(wexp, aexp, H / 2, bpr, 2 * I, n_base, c, c < cpr, wq[st],
                               av[st]);
     }
     stage.store(s_x, 0);
@@ -908,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(const float* __restrict__
 #pragma unroll
   for (int st = 0; st < STD; ++st) {
     const int c = tl + st * LD;
-    load_weights<NUD, AbsT>(wexp, aexp, (size_t)I / 2, bpr, H, n_base, c, c < cpr, wq[st], av[st]);
+    load_weights<NUD, AbsT>(wexp, aexp, I / 2, bpr, H, n_base, c, c < cpr, wq[st], av[st]);
   }
   // One poller per workgroup, on its XCD's ready line, about every 0.25 us
   // (the first poll returns after the weight loads: loads complete in order).
@@ -1044,6 +1083,8 @@ static DecodeKArgs decode_args(const GemmArgs& g, const DecodePlan& p) {
   a.slot_div = g.slot_div;
   a.rows_max_decode = g.rows_max_decode;
   a.route_k = 0;
+  a.vec_out = p.S == 1 && p.R == 1 && (p.NU == 2 || p.NU == 4) && g.N % p.NU == 0 &&
+              reinterpret_cast<uintptr_t>(g.y) % (2 * p.NU) == 0;
   a.S = p.S;
   a.cps = p.cps;
   a.cpr = g.K / 32;
@@ -1066,7 +1107,7 @@ hipError_t launch_decode_routed(const GemmArgs& g, const DecodePlan& p, const fl
   DecodeKArgs a = decode_args(g, p);
   a.route_logits = logits;
   a.ro = ro;
-  a.route_k = ro.K;
+  a.route_k = (int16_t)ro.K;
   if (ro.E > 2 * kWave) return hipErrorInvalidValue;
   const bool two = ro.E > kWave;
   hipError_t err;
