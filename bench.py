@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--ceilings", default="",
                     help="measure the machine ceilings (pure-read GB/s against size, empty "
                          "launch, matrix-core clock, vendor fp16 GEMM) into this JSONL")
+    ap.add_argument("--timeline", default="",
+                    help="per-wavefront phase timeline of the OLMoE-shaped decode launches from "
+                         "the instrumented build (libgnf4_timeline.so) into this JSONL")
     ap.add_argument("--absmax-dtype", choices=("f32", "bf16"), default="f32",
                     help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
     ap.add_argument("--only", default="",
@@ -679,6 +682,74 @@ def measure_ceilings(path, dev, replays=5):
     return recs
 
 
+def measure_timeline(path, dev, name="olmoe", launches=(0, 17, 33)):
+    """Phase timeline of single cold decode launches (routed gate_up, then
+    down) from the instrumented build: per wavefront the real-time counter
+    (100 MHz) at start, expert known, first weight data used, rows decoded
+    and reduced, outputs stored.  The XCDs' counters are not aligned with
+    each other, so times are taken relative to each XCD's first wavefront;
+    the percentiles are over all wavefronts of the launch (us)."""
+    import ctypes
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    wl = wls.WORKLOADS[name]
+    L = wl.layers
+    layers = build_layers(wl, L, dev) + build_layers(wl, L, dev, L) + \
+        build_layers(wl, L, dev, 2 * L)
+    lib = gnf4.library()
+    lib.exp_get_timeline.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.exp_get_timeline.restype = ctypes.c_int
+    lib.exp_clear_timeline.restype = ctypes.c_int
+    for ly in layers:
+        run_layer(wl, ly)
+    torch.cuda.synchronize()
+
+    def down(ly):
+        r = ly.route.result
+        gnf4.grouped_gemm(ly.xd, ly.pd, ly.ad, r.group_sizes, r.group_expert_ids, G=ly.G,
+                          y=ly.yd, workspace=ly.wsd)
+
+    def pct(v):
+        return [round(float(np.percentile(v, q)), 2) for q in (10, 50, 90)]
+
+    out = open(path, "w") if path else None
+    for gemm, fn in (("gate_up", lambda ly: gate_up(wl, ly)), ("down", down)):
+        for li in launches:
+            for k in range(1, len(layers)):  # every other layer first: layer li is cold
+                fn(layers[(li + k) % len(layers)])
+            torch.cuda.synchronize()
+            assert lib.exp_clear_timeline() == 0
+            fn(layers[li])
+            torch.cuda.synchronize()
+            buf = np.zeros(8192 * 8, np.uint64)
+            assert lib.exp_get_timeline(buf.ctypes.data, buf.nbytes) == 0
+            t = buf.reshape(8192, 8)
+            t = t[t[:, 4] != 0].astype(np.int64)
+            xcc = t[:, 7] & 0xF
+            rel = np.zeros((len(t), 5))
+            spans = []
+            for x in np.unique(xcc):
+                sel = xcc == x
+                base = t[sel, 0].min()
+                rel[sel] = (t[sel, :5] - base) / 100.0
+                spans.append(float(rel[sel, 4].max()))
+            rec = {"workload": name, "gemm": gemm, "layer": li, "waves": int(len(t)),
+                   "start": pct(rel[:, 0]),
+                   "start_to_expert": pct(rel[:, 1] - rel[:, 0]),
+                   "expert_to_first_data": pct(rel[:, 2] - rel[:, 1]),
+                   "first_data_to_decoded": pct(rel[:, 3] - rel[:, 2]),
+                   "decoded_to_stored": pct(rel[:, 4] - rel[:, 3]),
+                   "wave": pct(rel[:, 4] - rel[:, 0]),
+                   "xcd_span_median": round(float(np.median(spans)), 2),
+                   "xcd_span_max": round(float(np.max(spans)), 2)}
+            print(json.dumps(rec), flush=True)
+            if out:
+                out.write(json.dumps(rec) + "\n")
+    if out:
+        out.close()
+
+
 def time_glue(path, dev, reps=10):
     """gnf4_swiglu and gnf4_combine alone at the decode (OLMoE, T=1) and
     prefill (DSV3, T=4096) shapes of the MoE layer: back-to-back launches
@@ -1072,7 +1143,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     special = (args.glue or args.cells or args.dgrad or args.mxfp4 or args.copy_mb or
-               args.dominant_only or args.ceilings)
+               args.dominant_only or args.ceilings or args.timeline)
     if not special and not args.child:
         parent_main(args)
         return
@@ -1082,6 +1153,9 @@ def main():
     from grouped_nf4_expert_amd import workloads as wls
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.timeline:
+        from grouped_nf4_expert_amd import timeline_build
+        gnf4.LIB_PATH = timeline_build.TL_LIB  # the phase-stamped build, this mode only
     gnf4.library()
     dev = torch.device("cuda:0")
 
@@ -1091,6 +1165,9 @@ def main():
         return
     if args.ceilings:
         measure_ceilings(args.ceilings, dev)
+        return
+    if args.timeline:
+        measure_timeline(args.timeline, dev, args.workload)
         return
     if args.cells:
         time_cells(dev, only or CELL_NAMES, args.cells)

@@ -69,8 +69,9 @@ def _link(objs, lib, extra=()):
     os.replace(tmp, lib)
 
 
-def build(verbose=False, extra_compile=(), extra_link=()):
-    """Compile every source and link both libraries.  extra_compile /
+def build(verbose=False, extra_compile=(), extra_link=(), timeline=True):
+    """Compile every source and link the libraries (with `timeline`, also the
+    phase-stamped diagnostic build, timeline_build.py).  extra_compile /
     extra_link: further hipcc flags (build_sanitized.py passes host-only
     sanitizer flags)."""
     os.makedirs(BUILD, exist_ok=True)
@@ -81,6 +82,9 @@ def build(verbose=False, extra_compile=(), extra_link=()):
     _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB, extra_link)
     if verbose:
         print(f"built {LIB} and {CEIL_LIB}")
+    if timeline:
+        from grouped_nf4_expert_amd import timeline_build
+        timeline_build.build(verbose)
     return LIB
 
 

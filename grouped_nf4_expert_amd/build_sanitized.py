@@ -24,5 +24,5 @@ LINK_SANITIZE = ["-shared-libasan", "-Xarch_host", "-fsanitize=address", "-Xarch
 
 
 if __name__ == "__main__":
-    _b.build(verbose=True, extra_compile=HOST_SANITIZE, extra_link=LINK_SANITIZE)
+    _b.build(verbose=True, extra_compile=HOST_SANITIZE, extra_link=LINK_SANITIZE, timeline=False)
     sys.exit(0)
