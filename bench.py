@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--timeline", default="",
                     help="per-wavefront phase timeline of the OLMoE-shaped decode launches from "
                          "the instrumented build (libgnf4_timeline.so) into this JSONL")
+    ap.add_argument("--ffn", default="",
+                    help="time the one-launch expert FFN (gnf4_moe_ffn_one_token) against the "
+                         "separate launches, per decode workload it serves, into this JSONL")
     ap.add_argument("--absmax-dtype", choices=("f32", "bf16"), default="f32",
                     help="block absmax of the packed stacks (bf16: 4.25 bits per weight)")
     ap.add_argument("--only", default="",
@@ -750,6 +753,62 @@ def measure_timeline(path, dev, name="olmoe", launches=(0, 17, 33)):
         out.close()
 
 
+def time_ffn(path, dev, names=("olmoe", "qwen3_t1", "gptoss"), replays=7):
+    """One decode layer as one launch (route/sort + gate_up + SwiGLU + down,
+    gnf4_moe_ffn_one_token) against the separate launches of the default
+    step (route/sort + gate_up, then down): per-layer time over 3 x L layers
+    of distinct cold weights, HIP events around graph replays, median."""
+    import torch
+    from grouped_nf4_expert_amd import gnf4
+    from grouped_nf4_expert_amd import workloads as wls
+    out = open(path, "w") if path else None
+    for name in names:
+        wl = wls.WORKLOADS[name]
+        H, N = wl.gemm("gate_up")
+        I = N // 2
+        rec = {"workload": name, "E": wl.E, "top_k": wl.top_k, "H": H, "I": I}
+        if not gnf4.moe_ffn_one_token_supported(wl.E, wl.top_k, H, I):
+            rec["fused"] = "not offered (its workgroups do not fit on the device at once)"
+        else:
+            L = wl.layers
+            layers = build_layers(wl, L, dev) + build_layers(wl, L, dev, L) + \
+                build_layers(wl, L, dev, 2 * L)
+            ws = gnf4.moe_ffn_one_token_workspace(wl.top_k, dev)
+            hs = [torch.empty((wl.top_k, I), dtype=torch.bfloat16, device=dev) for _ in layers]
+
+            def fused():
+                for ly, h in zip(layers, hs):
+                    gnf4.moe_ffn_one_token(ly.logits, ly.x, (ly.pg, ly.ag), (ly.pd, ly.ad),
+                                           wl.top_k, buffers=ly.route, h=h, y=ly.yd, workspace=ws)
+
+            def separate():
+                for ly in layers:
+                    run_layer(wl, ly)
+
+            for label, fn in (("separate_us_per_layer", separate), ("fused_us_per_layer", fused)):
+                g = capture(fn)
+                g.replay()
+                torch.cuda.synchronize()
+                us = []
+                for _ in range(replays):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    g.replay()
+                    b.record()
+                    torch.cuda.synchronize()
+                    us.append(a.elapsed_time(b) * 1e3 / len(layers))
+                rec[label] = round(sorted(us)[len(us) // 2], 3)
+                del g
+            rec["workspace_clear_after"] = bool((ws.view(torch.int32) == 0).all().item())
+            del layers
+            torch.cuda.empty_cache()
+        print(f"[ffn] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        if out:
+            out.write(json.dumps(rec) + "\n")
+    if out:
+        out.close()
+
+
 def time_glue(path, dev, reps=10):
     """gnf4_swiglu and gnf4_combine alone at the decode (OLMoE, T=1) and
     prefill (DSV3, T=4096) shapes of the MoE layer: back-to-back launches
@@ -1143,7 +1202,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     special = (args.glue or args.cells or args.dgrad or args.mxfp4 or args.copy_mb or
-               args.dominant_only or args.ceilings or args.timeline)
+               args.dominant_only or args.ceilings or args.timeline or args.ffn)
     if not special and not args.child:
         parent_main(args)
         return
@@ -1168,6 +1227,9 @@ def main():
         return
     if args.timeline:
         measure_timeline(args.timeline, dev, args.workload)
+        return
+    if args.ffn:
+        time_ffn(args.ffn, dev)
         return
     if args.cells:
         time_cells(dev, only or CELL_NAMES, args.cells)
