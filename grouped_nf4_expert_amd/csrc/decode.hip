@@ -847,10 +847,11 @@ __device__ __forceinline__ void ffn_rows(const float4* s_x, int plane, const flo
   for (int j = 0; j < NU; ++j) acc[j] = team_sum<L>(acc[j]);
 }
 
-// At most 64 VGPRs (eight wavefronts per SIMD): eight workgroups per CU, so
-// the OLMoE- and Qwen3-shaped launches fit on the device at once.
+// At most 80 VGPRs (six wavefronts per SIMD): six workgroups per CU, so the
+// OLMoE-shaped launch (1,536 workgroups) and the Qwen3-shaped one (1,280)
+// fit on the device at once.
 template <int LG, int NUG, int STG, int LD, int NUD, int STD, typename AbsT, int EPL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void ffn_kernel(const float* __restrict__ k_logits,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void ffn_kernel(const float* __restrict__ k_logits,
                                                        const uint16_t* __restrict__ k_x, int k_E,
                                                        FfnKArgs a) {
   __shared__ float s_lut[32];
@@ -871,7 +872,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     t = local - j * tiles;
     return PickQuery{a.route_k, j};
   };
-  const int expert = route_pick<EPL>(k_logits, k_E, lane, wg == 0 && wave == 0, a.ro, place);
+  // wavefront 0 routes for the workgroup; the others place themselves and
+  // read its expert from LDS
+  __shared__ int s_expert;
+  if (wave == 0) {
+    const int e = route_pick<EPL>(k_logits, k_E, lane, wg == 0, a.ro, place);
+    if (lane == 0) s_expert = e;
+  } else {
+    place();
+  }
+  __syncthreads();
+  const int expert = s_expert;
   if (lane < 16) s_lut[2 * lane] = nf4_level(lane);
   const float* lut = s_lut;
   const int H = a.H, I = a.I, K = a.route_k;
@@ -1156,10 +1167,21 @@ hipError_t launch_decode(const GemmArgs& g, const DecodePlan& p, hipStream_t str
 // ------------------------------------------------------------ fused FFN
 // The FFN launch's two roles take the plans the one-token decode launches
 // would (no K split); the kernel is instantiated for the role pairs below.
+// The one-token decode plans of the two projections, with the most rows per
+// lane their steps allow (NU * steps <= 4): fewer, fatter workgroups, so the
+// launch fits on the device at once and fewer down workgroups wait.
+static DecodePlan ffn_role_plan(int top_k, int64_t N, int64_t K, int num_cus) {
+  DecodePlan p = plan_decode(top_k, N, K, top_k, 1, num_cus);
+  if (p.L == 0) return p;
+  p.NU = kMaxLoads / p.steps;
+  p.rows_per_block = kWaves * (kWave / p.L) * p.NU;
+  p.n_tiles = (int)((N + p.rows_per_block - 1) / p.rows_per_block);
+  return p;
+}
+
 bool plan_ffn(int64_t E, int top_k, int64_t H, int64_t I, int num_cus, FfnPlan& out) {
-  (void)E;
-  out.gu = plan_decode(top_k, 2 * I, H, top_k, 1, num_cus);
-  out.dn = plan_decode(top_k, H, I, top_k, 1, num_cus);
+  out.gu = ffn_role_plan(top_k, 2 * I, H, num_cus);
+  out.dn = ffn_role_plan(top_k, H, I, num_cus);
   const DecodePlan& g = out.gu;
   const DecodePlan& d = out.dn;
   if (g.L == 0 || d.L == 0 || g.S != 1 || d.S != 1 || g.R != 1 || d.R != 1) return false;
@@ -1180,9 +1202,8 @@ namespace {
 
 // role plans (L, NU, steps) the kernel is built for, as pairs
 #define GNF4_FFN_PAIRS(X)                  \
-  X(64, 4, 1, 32, 2, 1) /* OLMoE   */     \
-  X(64, 2, 1, 8, 1, 3)  /* Qwen3   */     \
-  X(32, 1, 3, 32, 1, 3) /* GPT-OSS */
+  X(64, 4, 1, 32, 4, 1) /* OLMoE   */     \
+  X(64, 4, 1, 8, 1, 3)  /* Qwen3   */
 
 template <int LG, int NUG, int STG, int LD, int NUD, int STD, typename AbsT, int EPL>
 hipError_t launch_ffn_one(const float* logits, const uint16_t* x, int E, const FfnKArgs& a,

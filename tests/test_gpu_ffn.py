@@ -113,8 +113,8 @@ def test_ffn_one_token_workloads(name):
 
 
 def test_ffn_one_token_refuses_what_does_not_fit_at_once():
-    # GPT-OSS-120B's layer needs 4320 workgroups: more than the device holds
-    # at once, so the fused launch is not offered for it
+    # GPT-OSS-120B's layer needs more workgroups than the device holds at
+    # once, so the fused launch is not offered for it
     wl = wls.WORKLOADS["gptoss"]
     H, N = wl.gemm("gate_up")
     assert not gnf4.moe_ffn_one_token_supported(wl.E, wl.top_k, H, N // 2)
