@@ -271,8 +271,16 @@ static gnf4_status gemm_common(const uint16_t* x, const uint8_t* packed, const v
   } else {
     a.rows_max_decode = kDecodeMaxRows;
     a.rows_min_tile = kDecodeMaxRows + 1;
-    // no group can exceed M rows: skip the tile launch when M is small
-    if (M <= kDecodeMaxRows) run_tile = false;
+    // No group can exceed M rows, and with the gather fused a group of a
+    // top-k routing holds at most T rows (a token picks each expert once).
+    // Then the decode launch serves every group, whatever its size (a group
+    // that breaks that bound is still computed, on the decode path), and
+    // the tile launch and its staging are skipped.
+    if (M <= kDecodeMaxRows || (slots && T <= kDecodeMaxRows)) {
+      a.rows_max_decode = INT_MAX;
+      a.rows_min_tile = INT_MAX;
+      run_tile = false;
+    }
   }
   const hipStream_t s = (hipStream_t)stream;
   if (validate_requested()) {
@@ -335,14 +343,11 @@ gnf4_status gnf4_gather_rows(const uint16_t* x, int64_t T, int64_t K, const int3
   return e == hipSuccess ? GNF4_OK : hip_fail(e);
 }
 
-// The dgrad's matrix-core path reads dy in 16-byte chunks.
-static bool dgrad_tile_ok(const uint16_t* dy, int64_t N) { return N % 8 == 0 && aligned(dy, 16); }
-
 // Path of a dgrad call: 2 = tile, 1 = GEMV.  Automatic: a batch averaging
-// at least 32 rows per group (prefill) takes the tile path when dy's layout
-// allows it; the GEMV path re-reads the weights once per 4 rows of dy.
-static int dgrad_path(int32_t path, int64_t M, int64_t G, bool tile_ok) {
-  if (path == 0) return auto_tile_only(M, G) && tile_ok ? 2 : 1;
+// at least 32 rows per group (prefill) takes the tile path; the GEMV path
+// re-reads the weights once per 4 rows of dy.
+static int dgrad_path(int32_t path, int64_t M, int64_t G) {
+  if (path == 0) return auto_tile_only(M, G) ? 2 : 1;
   return path;
 }
 
@@ -350,7 +355,7 @@ size_t gnf4_grouped_dgrad_workspace_size_ex(int64_t M, int64_t N, int64_t K, int
                                             int64_t E, int32_t path) {
   (void)E;
   if (M <= 0 || N <= 0 || K < kBlock || G <= 0) return 0;
-  if (dgrad_path(path, M, G, N % 8 == 0) == 2) return stage_bytes(M, N);
+  if (dgrad_path(path, M, G) == 2) return stage_bytes(M, N);
   return dgrad_workspace_bytes(plan_dgrad(M, N, K, G, device_cu_count()), M, K);
 }
 
@@ -403,10 +408,8 @@ gnf4_status gnf4_grouped_dgrad_ex(const uint16_t* dy, const uint8_t* packed, con
     if (ve != hipSuccess) return hip_fail(ve);
     if (bad) return GNF4_ERR_INVALID_ARG;
   }
-  const bool tile_ok = dgrad_tile_ok(dy, N);
-  const int run = dgrad_path(path, M, G, tile_ok);
+  const int run = dgrad_path(path, M, G);
   if (run == 2) {
-    if (!tile_ok) return GNF4_ERR_UNSUPPORTED;  // forced tile path, dy not in 16-byte chunks
     if (!workspace || workspace_bytes < stage_bytes(M, N)) return GNF4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return GNF4_ERR_INVALID_ARG;
     if (!is_device_ptr(workspace)) return GNF4_ERR_NOT_DEVICE_PTR;

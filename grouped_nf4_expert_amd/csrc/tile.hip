@@ -818,7 +818,14 @@ __global__ __launch_bounds__(kDgThreads, 1) void dgrad_tile_kernel(DgradTileKArg
 // and exact in fp16 down to 2^-14, i.e. for every value within 2^28 of the
 // row's largest; smaller ones round to fp16's subnormals (nearest, ties to
 // even).  Elements past the row's end up to the padded width are zeros.
+// Rows are read 16 bytes at a time when every row starts 16-byte aligned
+// (K % 8 == 0 and an aligned x), else element by element (a dgrad's dy of
+// any width N).  Beside a decode launch (groups of up to 8 rows there, the
+// larger ones here) the staging first looks at the group sizes and, when no
+// group has enough rows for the tile kernel to take it, stages nothing: the
+// tile kernel then finds no group and reads no staged row.
 constexpr int kStageThreads = 256;
+constexpr int kStageGateMaxGroups = 4096;  // sizes scanned per wavefront at most
 
 struct StageKArgs {
   const uint16_t* x;
@@ -828,6 +835,9 @@ struct StageKArgs {
   bool gather_rows;      // rows are output rows read through `slots`
   int K, ld;
   bool natural;          // natural K order (else the NF4 decode's slot order)
+  bool vec;              // 16-byte row loads (K % 8 == 0, x 16-byte aligned)
+  const int32_t* gate_sizes;  // non-null: stage only if some gate_sizes[g] >= gate_min
+  int gate_G, gate_min;
   uint16_t* xh;
   int32_t* row_exp;
 };
@@ -837,10 +847,29 @@ __device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// Elements 8c .. 8c + 7 of a row as four bf16 pairs, zeros past element K.
+__device__ __forceinline__ uint4 load8(const uint16_t* row, int c, int K, bool vec) {
+  if (vec) return reinterpret_cast<const uint4*>(row)[c];
+  uint32_t d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 8 * c + 2 * j;
+    const uint32_t lo = e < K ? row[e] : 0u;
+    const uint32_t hi = e + 1 < K ? row[e + 1] : 0u;
+    d[j] = lo | (hi << 16);
+  }
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
 __global__ __launch_bounds__(kStageThreads) void stage_x_kernel(StageKArgs s) {
   const int lane = threadIdx.x % kWave;
   const int waves = gridDim.x * (kStageThreads / kWave);
-  const int chunks = s.K / 8;
+  const int chunks = (s.K + 7) / 8;
+  if (s.gate_sizes) {
+    bool hit = false;
+    for (int g = lane; g < s.gate_G; g += kWave) hit = hit || s.gate_sizes[g] >= s.gate_min;
+    if (__builtin_amdgcn_ballot_w64(hit) == 0) return;  // the same answer in every wavefront
+  }
   for (int r = blockIdx.x * (kStageThreads / kWave) + threadIdx.x / kWave; r <= s.rows;
        r += waves) {
     int src = r < s.rows ? r : -1;
@@ -848,7 +877,7 @@ __global__ __launch_bounds__(kStageThreads) void stage_x_kernel(StageKArgs s) {
       const int slot = s.slots[r];
       src = (slot >= 0 && slot < s.T * s.slot_div) ? slot / s.slot_div : -1;
     }
-    const uint4* row = reinterpret_cast<const uint4*>(s.x + (size_t)(src >= 0 ? src : 0) * s.K);
+    const uint16_t* row = s.x + (size_t)(src >= 0 ? src : 0) * s.K;
     uint32_t mb = 0;
     if (src >= 0) {
       for (int c0 = lane; c0 < chunks; c0 += 4 * kWave) {
@@ -856,7 +885,7 @@ __global__ __launch_bounds__(kStageThreads) void stage_x_kernel(StageKArgs s) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int cc = c0 + u * kWave;
-          v[u] = row[cc < chunks ? cc : lane % chunks];
+          v[u] = load8(row, cc < chunks ? cc : lane % chunks, s.K, s.vec);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -872,7 +901,7 @@ __global__ __launch_bounds__(kStageThreads) void stage_x_kernel(StageKArgs s) {
     uint4* out = reinterpret_cast<uint4*>(s.xh + (size_t)r * s.ld);
     for (int c = lane; c < s.ld / 8; c += kWave) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (src >= 0 && c < chunks) v = row[c];
+      if (src >= 0 && c < chunks) v = load8(row, c, s.K, s.vec);
       const uint32_t d[4] = {v.x, v.y, v.z, v.w};
       float f[8];
 #pragma unroll
@@ -927,6 +956,13 @@ hipError_t launch_stage_x(const GemmArgs& g, const StagePlan& p, bool natural_or
   s.K = g.K;
   s.ld = p.ld;
   s.natural = natural_order;
+  s.vec = g.K % 8 == 0 && reinterpret_cast<uintptr_t>(g.x) % 16 == 0;
+  // the tile kernel takes groups of rows_min_tile rows or more; with
+  // rows_min_tile <= 1 it takes every group and the staging always runs
+  const bool gate = g.rows_min_tile > 1 && g.G <= kStageGateMaxGroups;
+  s.gate_sizes = gate ? g.sizes : nullptr;
+  s.gate_G = g.G;
+  s.gate_min = g.rows_min_tile;
   s.xh = g.xh;
   s.row_exp = g.row_exp;
   const int per_block = kStageThreads / kWave;

@@ -351,14 +351,14 @@ gnf4_status gnf4_grouped_gemm_mxfp4(const uint16_t* x, int64_t T, const int32_t*
  *    its largest absmax over the N rows in [2^14, 2^15)), dy rows staged
  *    once in fp16 with a power of two per row (putting the row's largest in
  *    [2^14, 2^15)), fp16 x fp16 -> fp32 MFMA, the scales applied exactly at
- *    the end.  Needs N % 8 == 0 and a 16-byte aligned dy.  Range: a block
+ *    the end; any N, dy 2-byte aligned.  Range: a block
  *    whose absmax lies within 2^25 of its column block's largest, and a dy
  *    value within 2^28 of its row's largest, enter the product with fp16's
  *    full precision; values further down round to fp16 subnormals (and
  *    below 2^-24 of the staged scale, to zero).
  * gnf4_grouped_dgrad chooses automatically: the tile path for a batch
- * averaging at least 32 rows per group (M >= 32 min(G, M)) when dy allows
- * it, else the GEMV path.
+ * averaging at least 32 rows per group (M >= 32 min(G, M)), else the GEMV
+ * path.
  * Limits: as gnf4_grouped_gemm, plus M * N < 2^31.
  * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE
  * (tile path without room for its exponents), GNF4_ERR_UNSUPPORTED,
@@ -375,8 +375,8 @@ gnf4_status gnf4_grouped_dgrad(const uint16_t* dy, const uint8_t* packed, const 
 /*
  * gnf4_grouped_dgrad_ex -- gnf4_grouped_dgrad with the path choice exposed,
  * for tests and tuning.  `path`: 0 = automatic (as gnf4_grouped_dgrad),
- * 1 = GEMV path, 2 = tile path (GNF4_ERR_UNSUPPORTED unless N % 8 == 0 and
- * dy is 16-byte aligned).  The workspace query takes the same `path`.
+ * 1 = GEMV path, 2 = tile path.  The workspace query takes the same
+ * `path`.
  */
 size_t gnf4_grouped_dgrad_workspace_size_ex(int64_t M, int64_t N, int64_t K, int64_t G,
                                             int64_t E, int32_t path);
@@ -479,14 +479,18 @@ gnf4_status gnf4_combine(const uint16_t* y, const int32_t* slot_rows, const floa
  * run.  The automatic choice: groups of up to 8 rows
  * take the decode path and larger ones the tile path, except that a batch
  * averaging at least 32 rows per group (M >= 32 min(G, M), prefill) runs
- * every group on the tile path and launches no decode kernel.
+ * every group on the tile path and launches no decode kernel, and that with
+ * the gather fused and T <= 8 tokens (a top-k routing then puts at most T
+ * rows in a group) the decode path serves every group, of any size, and no
+ * tile launch runs.
  *
  * Limits: M >= 0, G >= 0 (either 0: nothing to do), E, N >= 1, K >= 64 with
  * K % 64 == 0, N * K/2 and M * K below 2^31 elements per expert and call,
  * G < 65536.  The decode path keeps one K split of an activation row in LDS,
  * at most 319 chunks of 32 (K <= 10208 unsplit); a larger K is split across
  * workgroups, which needs the workspace.  Whenever the tile path may run
- * (M > 8, or path 2 of the _ex form) the workspace is required.
+ * (M > 8 unless the gather is fused with T <= 8, or path 2 of the _ex form)
+ * the workspace is required.
  * Errors: GNF4_ERR_INVALID_ARG, GNF4_ERR_NOT_DEVICE_PTR, GNF4_ERR_WORKSPACE
  * (workspace missing or smaller than the size query returns; also: K too
  * large to run unsplit and no workspace given),

@@ -25,11 +25,6 @@ pytestmark = pytest.mark.gpu
 DEC, TILE, AUTO = gnf4.PATH_DECODE, gnf4.PATH_TILE, gnf4.PATH_AUTO
 
 
-def _skip_tile(path, N):
-    if path == TILE and N % 8:
-        pytest.skip("the tile path reads dy in 16-byte chunks (N % 8 == 0)")
-
-
 def _oracle_stack(wl, host, N, K):
     p = np.zeros((wl.E, N, K // 2), np.uint8)
     a = np.zeros((wl.E, N, K // 64), np.float32)
@@ -45,7 +40,6 @@ def _oracle_stack(wl, host, N, K):
 def test_dgrad_workload_shapes(name, gemm, path):
     wl = wls.WORKLOADS[name]
     K, N = wl.gemm(gemm)
-    _skip_tile(path, N)
     logits = wls.router_logits(wl)
     ref = oracle.ref_route_sort(logits, wl.top_k)
     r = gnf4.route_sort(torch.from_numpy(logits).to(DEV), wl.top_k)
@@ -95,12 +89,27 @@ def _run(c, workspace=None, path=AUTO):
 @pytest.mark.parametrize("path", [AUTO, DEC, TILE])
 def test_dgrad_boundaries(case, path):
     E, N, K, sizes, ids, M = BOUNDARY_CASES[case]
-    _skip_tile(path, N)
     note(f"dgrad boundary {case} path={path}")
     c = _custom(E, N, K, sizes, ids, M, seed=21)
     dx = _run(c, path=path)
     if c["written"].any():
         check_gemm(dx, c["o"], c["written"], f"dgrad {case} path {path}")
+
+
+# The tile path stages dy rows of any width N, from a dy that is only 2-byte
+# aligned (element by element); a prefill-sized batch takes it automatically.
+@pytest.mark.parametrize("N", [1, 7, 301])
+@pytest.mark.parametrize("path", [AUTO, TILE])
+def test_dgrad_tile_any_width_unaligned_dy(N, path):
+    note(f"dgrad tile N={N} unaligned dy path={path}")
+    c = _custom(3, N, 256, [30, 34], [2, 0], 64, seed=N)
+    flat = torch.empty(64 * N + 1, dtype=torch.bfloat16, device=DEV)
+    dy = flat[1:].view(64, N)
+    dy.copy_(c["dy"])
+    assert dy.data_ptr() % 16 != 0
+    c["dy"] = dy
+    dx = _run(c, path=path)
+    check_gemm(dx, c["o"], c["written"], f"dgrad N={N} unaligned path {path}")
 
 
 # Rows of 10, 16, 24 and 32 chunks of 32 codes: the decode path's teams of

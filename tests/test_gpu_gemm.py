@@ -389,6 +389,33 @@ def test_fused_gather_bad_slots_skip_rows(path):
     check_gemm(full[1:M + 1], c["y_ref"], written, f"bad slots path {path}")
 
 
+# The automatic path beside the fused gather.  With T <= 8 tokens a top-k
+# routing puts at most T rows in a group, so the decode launch alone serves
+# every group, also a group of a caller-built grouping that breaks that bound
+# (12 rows of 4 tokens: duplicate picks).  With more tokens, groups of more
+# than 8 rows go to the tile launch ([10, 8]); when no group has that many
+# ([8, 8, 8]) the tile launch's staging stages nothing and the decode launch
+# serves them all.
+@pytest.mark.parametrize("T,top_k,sizes,ids", [(4, 4, [12, 4], [0, 2]),
+                                               (9, 2, [10, 8], [1, 0]),
+                                               (12, 2, [8, 8, 8], [2, 0, 1])])
+def test_fused_gather_auto_group_sizes(T, top_k, sizes, ids):
+    E, N, K = 3, 64, 256
+    M = sum(sizes)
+    assert M == T * top_k
+    rng = np.random.default_rng(T)
+    slots = rng.permutation(M).astype(np.int32)
+    x_tok = wls.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    x_rows = x_tok[slots // top_k]
+    c = _custom(E, N, K, sizes, ids, M, seed=35 + T, x=x_rows)
+    note(f"gemm fused gather auto T={T} top_k={top_k} sizes={sizes}")
+    y = gnf4.grouped_gemm(bf16_dev(x_tok), c["packed"], c["absmax"], c["sizes"], c["ids"],
+                          G=len(sizes), path=AUTO, sorted_slots=torch.from_numpy(slots).to(DEV),
+                          top_k=top_k)
+    torch.cuda.synchronize()
+    check_gemm(y, c["y_ref"], c["written"], f"fused gather auto T={T} sizes={sizes}")
+
+
 @pytest.mark.parametrize("split_k", [0, 2])
 def test_fused_gather_one_token(split_k):
     """A single token behind the fused gather (a batch-1 decode step): every

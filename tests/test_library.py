@@ -180,6 +180,21 @@ def test_dgrad_split_rule(lib):
     assert q(3, 1536, 2048, 3, 4) == 24 * 3 * 2048 * 4     # three rows, 24 splits
 
 
+def test_dgrad_tile_workspace_any_width(lib):
+    """A prefill-sized dgrad batch (M >= 32 G) plans the tile path for any
+    width N: its workspace is the staged dy, 4 (M + 1) bytes of exponents and
+    2 (M + 1) ceil128(N) fp16 bytes, each rounded up to 256."""
+    q = lib.gnf4_grouped_dgrad_workspace_size_ex
+    q.restype = ctypes.c_size_t
+    q.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32]
+    def staged(M, N):
+        up = lambda b: (b + 255) // 256 * 256
+        return up(4 * (M + 1)) + up(2 * (M + 1) * ((N + 127) // 128 * 128))
+    for N in (1, 7, 301, 2048):
+        assert q(64, N, 256, 2, 3, 0) == staged(64, N)
+        assert q(64, N, 256, 2, 3, 2) == staged(64, N)
+
+
 def test_no_cpu_fallback_in_binding():
     """The binding never routes through the oracle or a torch fallback."""
     src = open(os.path.join(ROOT, "grouped_nf4_expert_amd", "gnf4.py")).read()
