@@ -256,18 +256,32 @@ COLD_BYTES = 1 << 30  # distinct weight bytes each cell's launches cycle through
 CELL_NAMES = ("olmoe", "qwen3_t1", "qwen3_t8", "gptoss", "dsv3")
 
 
-def cell_plan(E, ng, N, K):
+def cell_plan(E, ng, N, K, scale_bytes_per_64=None):
     """Expert-id rotations and stack copies for one cold cell.  A launch
     reads the touched experts of one stack copy; the routed group sizes are
     kept and the expert ids moved by whole blocks of ng per rotation, so the
     rotations of one copy read disjoint experts, and the copies cycle at
     least COLD_BYTES of distinct weights before any byte is read again (the
-    Infinity Cache holds 256 MB)."""
-    per_expert = N * K // 2 + ABS_BYTES * N * K // 64
+    Infinity Cache holds 256 MB).  scale_bytes_per_64: scale bytes per 64
+    weights (the absmax width by default; 2 for MXFP4's byte per 32)."""
+    sb = ABS_BYTES if scale_bytes_per_64 is None else scale_bytes_per_64
+    per_expert = N * K // 2 + sb * N * K // 64
     rotations = max(1, E // max(ng, 1))
     cycle = rotations * ng * per_expert
     copies = max(1, -(-COLD_BYTES // cycle))
     return rotations, copies
+
+
+def rotated_ids(r, ng, E, rotations, dev):
+    """The routed group_expert_ids with the first ng entries moved by whole
+    blocks of ng, one id tensor per rotation (cell_plan)."""
+    import torch
+    sets = []
+    for q in range(rotations):
+        ids = r.group_expert_ids.clone()
+        ids[:ng] = (torch.arange(ng, device=dev, dtype=torch.int32) + q * ng) % E
+        sets.append(ids)
+    return sets
 
 
 def time_cells(dev, names=CELL_NAMES, path=None, min_decode=100, min_prefill=10):
@@ -313,11 +327,7 @@ def time_cells(dev, names=CELL_NAMES, path=None, min_decode=100, min_prefill=10)
             stacks = stack_cache[key]
             while len(stacks) < copies:  # byte-identical copies at other addresses
                 stacks.append((stacks[0][0].clone(), stacks[0][1].clone()))
-            id_sets = []
-            for q in range(rot):
-                ids = r.group_expert_ids.clone()
-                ids[:ng] = (torch.arange(ng, device=dev, dtype=torch.int32) + q * ng) % wl.E
-                id_sets.append(ids)
+            id_sets = rotated_ids(r, ng, wl.E, rot, dev)
             if gemm == "gate_up":
                 x = wls.activations_device(wl.T, K, dev, wl.seed, 50, K)
                 slots = r.sorted_slots
@@ -376,16 +386,18 @@ def time_cells(dev, names=CELL_NAMES, path=None, min_decode=100, min_prefill=10)
 
 
 def time_dgrad(path, dev, only=()):
-    """gnf4_grouped_dgrad alone, cycling over enough weight copies to defeat
-    the Infinity Cache (as the forward cells); per-launch HIP events over a
-    graph of back-to-back launches.  Algorithmic bytes as the forward GEMM
-    (each touched expert's codes and absmax once, dy read, dx written)."""
+    """gnf4_grouped_dgrad alone over cold weights as the forward cells
+    (cell_plan: rotated expert ids and stack copies, at least COLD_BYTES of
+    distinct touched weights per cycle); per-launch HIP events over a graph
+    of back-to-back launches.  Algorithmic bytes as the forward GEMM (each
+    touched expert's codes and absmax once, dy read, dx written)."""
     import torch
     from grouped_nf4_expert_amd import gnf4
     from grouped_nf4_expert_amd import workloads as wls
     out = open(path, "w")
-    cells = (("olmoe", "gate_up"), ("olmoe", "down"), ("qwen3_t8", "gate_up"),
-             ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"), ("dsv3", "gate_up"))
+    cells = (("olmoe", "gate_up"), ("olmoe", "down"), ("qwen3_t1", "gate_up"), ("qwen3_t1", "down"),
+             ("qwen3_t8", "gate_up"), ("gptoss", "gate_up"), ("gptoss", "down"), ("dsv3", "down"),
+             ("dsv3", "gate_up"))
     for name, gemm in cells:
         if only and name not in only:
             continue
@@ -395,28 +407,27 @@ def time_dgrad(path, dev, only=()):
         G = min(wl.E, wl.M)
         ng = int(r.num_groups.cpu()[0])
         K, N = wl.gemm(gemm)
-        stack_bytes = wl.E * (N * K // 2 + N * K // 16)
-        copies = max(1, min(8, int(np.ceil(600e6 / stack_bytes))))
-        stacks = []
-        for ci in range(copies):
-            p = torch.empty((wl.E, N, K // 2), dtype=torch.uint8, device=dev)
-            a = torch.empty((wl.E, N, K // 64), dtype=torch.float32, device=dev)
-            for e in range(wl.E):
-                gnf4.pack(wls.expert_weights_device(wl, gemm, e, dev, 200 + ci), out=(p[e], a[e]))
-            stacks.append((p, a))
+        rot, copies = cell_plan(wl.E, ng, N, K, scale_bytes_per_64=4)
+        p = torch.empty((wl.E, N, K // 2), dtype=torch.uint8, device=dev)
+        a = torch.empty((wl.E, N, K // 64), dtype=torch.float32, device=dev)
+        for e in range(wl.E):
+            gnf4.pack(wls.expert_weights_device(wl, gemm, e, dev, 200), out=(p[e], a[e]))
+        stacks = [(p, a)] + [(p.clone(), a.clone()) for _ in range(copies - 1)]
+        id_sets = rotated_ids(r, ng, wl.E, rot, dev)
         dy = wls.activations_device(wl.M, N, dev, wl.seed, 60, N)
         dx = torch.empty((wl.M, K), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(gnf4.library().gnf4_grouped_dgrad_workspace_size(wl.M, N, K, G, wl.E),
                              16), dtype=torch.uint8, device=dev)
-        per = 4 * copies if name != "dsv3" else 1
+        work = [(c, q) for c in range(copies) for q in range(rot)]
+        per = len(work)
 
         def launches():
-            for i in range(per):
-                p, a = stacks[i % copies]
-                gnf4.grouped_dgrad(dy, p, a, r.group_sizes, r.group_expert_ids, G=G, dx=dx,
+            for c, q in work:
+                p, a = stacks[c]
+                gnf4.grouped_dgrad(dy, p, a, r.group_sizes, id_sets[q], G=G, dx=dx,
                                    workspace=ws)
         graph = capture(launches)
-        reps = 10 if name != "dsv3" else 2
+        reps = max(3, -(-(2 if name == "dsv3" else 100) // per))
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
         graph.replay()
@@ -436,7 +447,8 @@ def time_dgrad(path, dev, only=()):
                "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
                "TFLOPs": round(flops / med / 1e6, 2),
                "mfma_frac": round(flops / med / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4),
-               "weight_copies": copies}
+               "launches_timed": per * reps, "weight_copies": copies, "id_rotations": rot,
+               "cold_cycle_bytes": copies * rot * ng * (N * K // 2 + N * K // 16)}
         out.write(json.dumps(rec) + "\n")
         out.flush()
         print(f"[dgrad] {json.dumps(rec)}", file=sys.stderr, flush=True)
@@ -470,27 +482,28 @@ def time_mxfp4(path, dev, only=()):
         G = min(wl.E, wl.M)
         ng = int(r.num_groups.cpu()[0])
         K, N = wl.gemm(gemm)
-        stack_bytes = wl.E * (N * K // 2 + N * K // 32)
-        copies = max(1, min(8, int(np.ceil(600e6 / stack_bytes))))
+        rot, copies = cell_plan(wl.E, ng, N, K, scale_bytes_per_64=2)
         gen = torch.Generator(device=dev).manual_seed(17)
-        stacks = [(torch.randint(0, 256, (wl.E, N, K // 2), dtype=torch.uint8, device=dev,
-                                 generator=gen),
-                   torch.randint(118, 131, (wl.E, N, K // 32), dtype=torch.uint8, device=dev,
-                                 generator=gen)) for _ in range(copies)]
+        p0 = torch.randint(0, 256, (wl.E, N, K // 2), dtype=torch.uint8, device=dev, generator=gen)
+        s0 = torch.randint(118, 131, (wl.E, N, K // 32), dtype=torch.uint8, device=dev,
+                           generator=gen)
+        stacks = [(p0, s0)] + [(p0.clone(), s0.clone()) for _ in range(copies - 1)]
+        id_sets = rotated_ids(r, ng, wl.E, rot, dev)
         x = wls.activations_device(wl.T, K, dev, wl.seed, 70, K)
         y = torch.empty((wl.M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(gnf4.gemm_workspace_size(wl.M, N, K, G, wl.E, path_sel), 16),
                          dtype=torch.uint8, device=dev)
-        per = copies if prefill else 4 * copies
+        work = [(c, q) for c in range(copies) for q in range(rot)]
+        per = len(work)
 
         def launches():
-            for i in range(per):
-                p, sc = stacks[i % copies]
-                gnf4.grouped_gemm_mxfp4(x, p, sc, r.group_sizes, r.group_expert_ids, G=G, y=y,
+            for c, q in work:
+                p, sc = stacks[c]
+                gnf4.grouped_gemm_mxfp4(x, p, sc, r.group_sizes, id_sets[q], G=G, y=y,
                                         workspace=ws, path=path_sel, sorted_slots=r.sorted_slots,
                                         top_k=wl.top_k)
         graph = capture(launches)
-        reps = 3 if prefill else 10
+        reps = max(3, -(-(10 if prefill else 100) // per))
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
         graph.replay()
@@ -511,7 +524,8 @@ def time_mxfp4(path, dev, only=()):
                "hbm_frac": round(byt / med / 1e3 / HBM_PEAK_GBS, 4),
                "TFLOPs": round(flops / med / 1e6, 2),
                "mfma_frac": round(flops / med / 1e6 / MFMA_FP16_PEAK_TFLOPS, 4),
-               "weight_copies": copies}
+               "launches_timed": per * reps, "weight_copies": copies, "id_rotations": rot,
+               "cold_cycle_bytes": copies * rot * ng * (N * K // 2 + N * K // 32)}
         out.write(json.dumps(rec) + "\n")
         out.flush()
         print(f"[mxfp4] {json.dumps(rec)}", file=sys.stderr, flush=True)

@@ -34,7 +34,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kNB = 8;          // weight rows in flight per wavefront
 constexpr int kChunkPitch = 33;  // floats per lane in the reduction buffer (conflict-free)
 
 struct DgradKArgs {
@@ -108,7 +107,8 @@ __device__ __forceinline__ bool find_row_group(const int32_t* sizes, const int32
 
 // L lanes (a team) cover L consecutive chunks of a weight row; the 64 / L
 // teams of a wavefront take different weight rows.
-template <int L, int R, typename AbsT>
+// kNB weight rows in flight per team and batch.
+template <int L, int R, int kNB, typename AbsT>
 __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradKArgs a) {
   constexpr int RPW = kWave / L;  // teams per wavefront
   __shared__ float s_lut[32];  // level q at index 2q (8-byte stride)
@@ -279,7 +279,10 @@ static int dgrad_lanes(int64_t cpr) {
 
 // Launch rule (host-known sizes only): R from the rows per group; the team
 // width L from K; N split so the grid holds about two wavefronts per SIMD,
-// each split at least one batch of rows per team.
+// each split at least one batch of rows per team.  Batches are 8 rows per
+// team, or 4 at one row of dy when 8 would allow at most half the splits
+// wanted (OLMoE and Qwen3 down: 16 splits, 128 workgroups, half the device;
+// with 4, 32 and 6-7% faster; Qwen3 gate_up, 24 of 32, ran 4% slower on 4).
 DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
   DgradPlan p;
   const int64_t g_eff = G < M ? G : M;
@@ -288,11 +291,15 @@ DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
   const int64_t cpr = K / 32;
   p.L = dgrad_lanes(cpr);
   p.k_tiles = (int)((cpr + p.L - 1) / p.L);
-  const int64_t rows_per_batch = (int64_t)kWaves * (kWave / p.L) * kNB;
   const int64_t target_waves = 8LL * num_cus;
   const int64_t per_split = (g_eff > 0 ? g_eff : 1) * p.k_tiles * kWaves;
   int64_t S = (target_waves + per_split - 1) / per_split;
-  const int64_t max_s = (N + rows_per_batch - 1) / rows_per_batch;
+  auto max_splits = [&](int nb) {
+    const int64_t rows_per_batch = (int64_t)kWaves * (kWave / p.L) * nb;
+    return (N + rows_per_batch - 1) / rows_per_batch;
+  };
+  p.NB = (p.R == 1 && 2 * max_splits(8) <= S) ? 4 : 8;
+  const int64_t max_s = max_splits(p.NB);
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
   p.rows_per_split = (int)((N + S - 1) / S);
@@ -300,22 +307,25 @@ DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
   return p;
 }
 
+template <int L, typename AbsT>
+static void launch_dgrad_LA(const DgradKArgs& a, int R, int NB, dim3 grid, hipStream_t stream) {
+  if (R == 1 && NB == 4)
+    hipLaunchKernelGGL((dgrad_kernel<L, 1, 4, AbsT>), grid, dim3(kThreads), 0, stream, a);
+  else if (R == 1)
+    hipLaunchKernelGGL((dgrad_kernel<L, 1, 8, AbsT>), grid, dim3(kThreads), 0, stream, a);
+  else if (R == 2)
+    hipLaunchKernelGGL((dgrad_kernel<L, 2, 8, AbsT>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dgrad_kernel<L, 4, 8, AbsT>), grid, dim3(kThreads), 0, stream, a);
+}
+
 template <int L>
-static void launch_dgrad_L(const DgradKArgs& a, bool abs_bf16, int R, dim3 grid,
+static void launch_dgrad_L(const DgradKArgs& a, bool abs_bf16, int R, int NB, dim3 grid,
                            hipStream_t stream) {
-  if (abs_bf16) {
-    switch (R) {
-      case 1: hipLaunchKernelGGL((dgrad_kernel<L, 1, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((dgrad_kernel<L, 2, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((dgrad_kernel<L, 4, uint16_t>), grid, dim3(kThreads), 0, stream, a); break;
-    }
-  } else {
-    switch (R) {
-      case 1: hipLaunchKernelGGL((dgrad_kernel<L, 1, float>), grid, dim3(kThreads), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((dgrad_kernel<L, 2, float>), grid, dim3(kThreads), 0, stream, a); break;
-      default: hipLaunchKernelGGL((dgrad_kernel<L, 4, float>), grid, dim3(kThreads), 0, stream, a); break;
-    }
-  }
+  if (abs_bf16)
+    launch_dgrad_LA<L, uint16_t>(a, R, NB, grid, stream);
+  else
+    launch_dgrad_LA<L, float>(a, R, NB, grid, stream);
 }
 
 size_t dgrad_workspace_bytes(const DgradPlan& p, int64_t M, int64_t K) {
@@ -342,10 +352,10 @@ hipError_t launch_dgrad(const DgradArgs& g, const DgradPlan& p, hipStream_t stre
   if (slots == 0) return hipSuccess;
   const dim3 grid((unsigned)p.k_tiles, slots, (unsigned)p.S);
   switch (p.L) {
-    case 64: launch_dgrad_L<64>(a, g.abs_bf16, p.R, grid, stream); break;
-    case 32: launch_dgrad_L<32>(a, g.abs_bf16, p.R, grid, stream); break;
-    case 16: launch_dgrad_L<16>(a, g.abs_bf16, p.R, grid, stream); break;
-    case 8: launch_dgrad_L<8>(a, g.abs_bf16, p.R, grid, stream); break;
+    case 64: launch_dgrad_L<64>(a, g.abs_bf16, p.R, p.NB, grid, stream); break;
+    case 32: launch_dgrad_L<32>(a, g.abs_bf16, p.R, p.NB, grid, stream); break;
+    case 16: launch_dgrad_L<16>(a, g.abs_bf16, p.R, p.NB, grid, stream); break;
+    case 8: launch_dgrad_L<8>(a, g.abs_bf16, p.R, p.NB, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -310,6 +310,7 @@ struct DgradPlan {
   int k_tiles;         // slices of K of L chunks of 32 (one chunk per lane)
   int S;               // N splits
   int rows_per_split;  // weight rows per split
+  int NB;              // weight rows in flight per team (8, or 4 to reach more splits)
 };
 DgradPlan plan_dgrad(int64_t M, int64_t N, int64_t K, int64_t G, int num_cus);
 size_t dgrad_workspace_bytes(const DgradPlan& p, int64_t M, int64_t K);

@@ -172,12 +172,19 @@ def test_dgrad_split_rule(lib):
     """The decode-path dgrad's N split, seen through its workspace size (fp32
     partials [S, M, K]) on a 256-CU device (the size a host without a device
     plans for): about two wavefronts per SIMD, each split at least one batch
-    of 8 rows per team; rows of 32 chunks use 32-lane teams, two per
-    wavefront, so OLMoE down splits 16 ways where 64-lane teams split 32."""
+    of 8 rows per team, or of 4 at one row of dy when batches of 8 would
+    allow at most half the splits wanted.  Rows of 32 chunks use 32-lane
+    teams, two per wavefront: batches of 8 would cap OLMoE down at 16 of 32
+    splits, so it takes batches of 4 and 32 splits, as OLMoE gate_up's
+    64-lane teams do with batches of 8; Qwen3's gate_up, capped at 24 of 32,
+    keeps batches of 8."""
     q = lib.gnf4_grouped_dgrad_workspace_size
     assert q(8, 2048, 2048, 8, 64) == 32 * 8 * 2048 * 4    # OLMoE gate_up: 64-lane teams
-    assert q(8, 2048, 1024, 8, 64) == 16 * 8 * 1024 * 4    # OLMoE down: 32-lane teams
-    assert q(3, 1536, 2048, 3, 4) == 24 * 3 * 2048 * 4     # three rows, 24 splits
+    assert q(8, 2048, 1024, 8, 64) == 32 * 8 * 1024 * 4    # OLMoE down: 32-lane teams
+    assert q(3, 1536, 2048, 3, 4) == 48 * 3 * 2048 * 4     # three rows, 48 splits
+    assert q(12, 1536, 2048, 4, 4) == 24 * 12 * 2048 * 4   # three rows per group: batches of 8
+    assert q(8, 1536, 2048, 8, 128) == 24 * 8 * 2048 * 4   # Qwen3 gate_up: 24 of 32, batches of 8
+    assert q(8, 2048, 768, 8, 128) == 32 * 8 * 768 * 4     # Qwen3 down: 16 of 32, batches of 4
 
 
 def test_dgrad_tile_workspace_any_width(lib):
