@@ -127,14 +127,30 @@ def test_dgrad_team_widths(K, sizes, ids, M):
     check_gemm(dx, c["o"], c["written"], f"dgrad K={K} sizes={sizes}")
 
 
-def test_dgrad_many_splits():
-    """Three one-row groups of K = 2048 over N = 1536 weight rows: the launch
-    rule splits N 24 ways, so the reduce sums two batches of split partials,
-    the second one padded."""
-    note("dgrad 24 N splits")
-    c = _custom(4, 1536, 2048, [1, 1, 1], [0, 2, 3], 3, seed=24)
+@pytest.mark.parametrize("sizes,M,splits", [([1, 1, 1], 3, 48), ([2, 2, 2], 6, 24)])
+def test_dgrad_many_splits(sizes, M, splits):
+    """Three groups of K = 2048 over N = 1536 weight rows.  One row each: the
+    launch rule takes batches of 4 weight rows per team and splits N 48 ways
+    (three full batches of split partials in the reduce).  Two rows each:
+    batches of 8 and 24 splits, so the reduce's second batch is padded."""
+    note(f"dgrad {splits} N splits, sizes {sizes}")
+    lib = gnf4.library()
+    assert lib.gnf4_grouped_dgrad_workspace_size(M, 1536, 2048, 3, 4) == splits * M * 2048 * 4
+    c = _custom(4, 1536, 2048, sizes, [0, 2, 3], M, seed=24 + M)
     dx = _run(c, workspace=None, path=DEC)
-    check_gemm(dx, c["o"], c["written"], "dgrad 24 splits")
+    check_gemm(dx, c["o"], c["written"], f"dgrad {splits} splits")
+
+
+def test_dgrad_ragged_splits_four_row_batches():
+    """Eight one-row groups of K = 1024 (32-lane teams) over N = 1000 weight
+    rows: batches of 4 rows per team, 16 splits of 63 rows, so every split
+    ends inside a batch and the last one holds 55 rows."""
+    note("dgrad ragged N=1000, batches of 4")
+    lib = gnf4.library()
+    assert lib.gnf4_grouped_dgrad_workspace_size(8, 1000, 1024, 8, 64) == 16 * 8 * 1024 * 4
+    c = _custom(8, 1000, 1024, [1] * 8, [5, 1, 7, 0, 3, 6, 2, 4], 8, seed=1000)
+    dx = _run(c, workspace=None, path=DEC)
+    check_gemm(dx, c["o"], c["written"], "dgrad ragged N=1000")
 
 
 def _absmax_scenarios(E, N, K):
