@@ -544,7 +544,9 @@ def ceilings_library():
     lib.gnf4_ceil_read.argtypes = [vp, ctypes.c_size_t, ci, vp, vp]
     lib.gnf4_ceil_empty.argtypes = [ci, vp]
     lib.gnf4_ceil_mfma.argtypes = [ci, ci, vp, vp, vp]
-    for f in (lib.gnf4_ceil_read, lib.gnf4_ceil_empty, lib.gnf4_ceil_mfma):
+    lib.gnf4_ceil_mfma_mix.argtypes = [ci, ci, ci, ci, vp, vp, vp]
+    for f in (lib.gnf4_ceil_read, lib.gnf4_ceil_empty, lib.gnf4_ceil_mfma,
+              lib.gnf4_ceil_mfma_mix):
         f.restype = ci
     return lib
 
@@ -564,7 +566,11 @@ def measure_ceilings(path, dev, replays=5):
     * empty launch: per-launch time of 1000 back-to-back empty kernels.
     * matrix cores: a v_mfma_f32_32x32x16_f16 loop on every SIMD, its
       TFLOP/s by HIP events and its shader clock from each wave's
-      s_memtime / s_memrealtime.
+      s_memtime / s_memrealtime, at 1, 2, 4 and 8 wavefronts per SIMD; then
+      the same loop (five chains per wavefront) with 0/4/8/12 dependent VALU
+      instructions and 0/1 LDS fragment reads per MFMA beside it, at 1 and 2
+      wavefronts per SIMD: the share of the matrix-core rate a kernel keeps
+      with that much other work per MFMA.
     * vendor fp16 GEMM (hipBLASLt through torch): 8192^3 and the
       DeepSeek-V3 expert shapes as a batch of 256 equal 128-row groups."""
     import ctypes
@@ -648,7 +654,7 @@ def measure_ceilings(path, dev, replays=5):
               "us_per_launch": round(timed(g, n), 3), "launches_per_replay": n})
         del g
 
-    for blocks, iters in ((1024, 200000), (2048, 100000)):
+    for blocks, iters in ((256, 800000), (512, 400000), (1024, 200000), (2048, 100000)):
         waves = blocks * 4
         stamps = torch.zeros(waves * 4, dtype=torch.int64, device=dev)
         sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
@@ -673,6 +679,35 @@ def measure_ceilings(path, dev, replays=5):
               "longest_wave_vs_event": round(float(wave_s.max()) * 1e3 / ms, 4),
               "peak_at_clock_TFLOPs": round(1024 * 32768 / 32 * ghz / 1e3, 1)})
         del stamps, sink
+
+    for wps in (1, 2):
+        blocks = 256 * wps
+        waves = blocks * 4
+        for valu, lds_reads in ((0, 0), (4, 0), (8, 0), (12, 0), (0, 1), (4, 1), (8, 1)):
+            iters = 2 * 10 ** 13 // (5 * 32768 * waves)  # about 8 ms at the published peak
+            stamps = torch.zeros(waves * 4, dtype=torch.int64, device=dev)
+            sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            evs = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                ok(lib.gnf4_ceil_mfma_mix(iters, blocks, valu, lds_reads,
+                                          ctypes.c_void_p(stamps.data_ptr()),
+                                          ctypes.c_void_p(sink.data_ptr()), st()), "mfma_mix")
+                b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            ms = evs[-1][0].elapsed_time(evs[-1][1])
+            t = stamps.cpu().numpy().reshape(waves, 4).astype(np.float64)
+            ghz = float(np.median((t[:, 1] - t[:, 0]) / ((t[:, 3] - t[:, 2]) / 100e6)) / 1e9)
+            flops = float(waves) * iters * 5 * 32768
+            tf = flops / ms / 1e9
+            emit({"ceiling": "mfma_f16_32x32x16_mixed", "waves_per_simd": wps, "chains": 5,
+                  "valu_per_mfma": valu, "lds_reads_per_mfma": lds_reads, "iters": iters,
+                  "ms": round(ms, 3), "TFLOPs": round(tf, 1),
+                  "shader_clock_GHz_median": round(ghz, 3),
+                  "frac_of_peak_at_clock": round(tf / (1024 * 32768 / 32 * ghz / 1e3), 4)})
+            del stamps, sink
 
     gen = torch.Generator(device=dev).manual_seed(7)
     cases = [("square", 1, 8192, 8192, 8192),

@@ -6,8 +6,9 @@
  * The pages ship a ceilings tool beside their kernel and a shape census
  * (page "grouped-nf4-gemm -- single-launch W4A16 GEMM over fused NF4 MoE
  * expert stacks", sections "Layout" and "Regenerate the machine-generated
- * artifacts").  This library is that tool's device half: three probe
- * kernels, each the simplest program that reaches one limit.  It is not part
+ * artifacts").  This library is that tool's device half: probe kernels,
+ * each the simplest program that reaches (or, for the mixed matrix-core
+ * loop, measures the share of) one limit.  It is not part
  * of the GEMM path and libgnf4 does not link it.
  *
  * Conventions: the same as gnf4.h.  Device pointers, caller-owned buffers,
@@ -55,6 +56,20 @@ gnf4_status gnf4_ceil_empty(int blocks, void* stream);
  * sums of one wave add up to 4 * iters * sum_k colsum_k(A) rowsum_k(B),
  * exactly while iters <= 256.  iters in [1, 2^24], blocks in [1, 65536]. */
 gnf4_status gnf4_ceil_mfma(int iters, int blocks, uint64_t* stamps, float* sink, void* stream);
+
+/* Matrix cores with work beside them: as gnf4_ceil_mfma, with five
+ * independent accumulator chains per wave (iters x 5 MFMAs), and after each
+ * MFMA `valu` dependent v_perm_b32 instructions (0, 4, 8 or 12: a decode-like
+ * chain) and, with lds_reads = 1, one 16-byte LDS read per lane that is the
+ * A operand of the same chain's next MFMA, five MFMAs later (a fragment read
+ * a step ahead; fixed conflict-free addresses).  The ratio of
+ * its TFLOP/s to gnf4_ceil_mfma's at the same clock is the share of the
+ * matrix-core rate a wave keeps with that much other work per MFMA.  stamps
+ * and sink as gnf4_ceil_mfma (sink values are not checkable here).
+ * GNF4_ERR_INVALID_ARG for other valu / lds_reads values or the limits of
+ * gnf4_ceil_mfma. */
+gnf4_status gnf4_ceil_mfma_mix(int iters, int blocks, int valu, int lds_reads, uint64_t* stamps,
+                               float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,12 +24,14 @@ def lib():
     h.gnf4_ceil_read.argtypes = [vp, ctypes.c_size_t, ci, vp, vp]
     h.gnf4_ceil_empty.argtypes = [ci, vp]
     h.gnf4_ceil_mfma.argtypes = [ci, ci, vp, vp, vp]
+    h.gnf4_ceil_mfma_mix.argtypes = [ci, ci, ci, ci, vp, vp, vp]
     return h
 
 
 def test_every_declared_symbol_is_exported(lib):
     declared = set(re.findall(r"\b(gnf4_ceil_\w+)\s*\(", open(HEADER).read()))
-    assert declared == {"gnf4_ceil_read", "gnf4_ceil_empty", "gnf4_ceil_mfma"}
+    assert declared == {"gnf4_ceil_read", "gnf4_ceil_empty", "gnf4_ceil_mfma",
+                        "gnf4_ceil_mfma_mix"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(gnf4_ceil_\w+)\b", out))
@@ -47,6 +49,11 @@ def test_bad_arguments_are_refused(lib):
     assert lib.gnf4_ceil_mfma(0, 1, fake, fake, None) == 1
     assert lib.gnf4_ceil_mfma(1, 1, None, fake, None) == 1
     assert lib.gnf4_ceil_mfma(1 << 25, 1, fake, fake, None) == 1
+    assert lib.gnf4_ceil_mfma_mix(1, 1, 6, 0, fake, fake, None) == 1    # valu not 0/4/8/12
+    assert lib.gnf4_ceil_mfma_mix(1, 1, 8, 2, fake, fake, None) == 1    # lds_reads not 0/1
+    assert lib.gnf4_ceil_mfma_mix(1, 0, 8, 1, fake, fake, None) == 1
+    assert lib.gnf4_ceil_mfma_mix(1, 1, 8, 1, None, fake, None) == 1
+    assert lib.gnf4_ceil_mfma_mix(0, 1, 8, 1, fake, fake, None) == 1
 
 
 @pytest.mark.gpu
