@@ -545,8 +545,9 @@ def ceilings_library():
     lib.gnf4_ceil_empty.argtypes = [ci, vp]
     lib.gnf4_ceil_mfma.argtypes = [ci, ci, vp, vp, vp]
     lib.gnf4_ceil_mfma_mix.argtypes = [ci, ci, ci, ci, vp, vp, vp]
+    lib.gnf4_ceil_mfma_split.argtypes = [ci, ci, ci, vp, vp, vp]
     for f in (lib.gnf4_ceil_read, lib.gnf4_ceil_empty, lib.gnf4_ceil_mfma,
-              lib.gnf4_ceil_mfma_mix):
+              lib.gnf4_ceil_mfma_mix, lib.gnf4_ceil_mfma_split):
         f.restype = ci
     return lib
 
@@ -570,7 +571,8 @@ def measure_ceilings(path, dev, replays=5):
       the same loop (five chains per wavefront) with 0/4/8/12 dependent VALU
       instructions and 0/1 LDS fragment reads per MFMA beside it, at 1 and 2
       wavefronts per SIMD: the share of the matrix-core rate a kernel keeps
-      with that much other work per MFMA.
+      with that much other work per MFMA; and MFMA-only wavefronts beside
+      VALU-only ones on the same SIMDs (4/8/12 dependent VALU per MFMA slot).
     * vendor fp16 GEMM (hipBLASLt through torch): 8192^3 and the
       DeepSeek-V3 expert shapes as a batch of 256 equal 128-row groups."""
     import ctypes
@@ -708,6 +710,27 @@ def measure_ceilings(path, dev, replays=5):
                   "shader_clock_GHz_median": round(ghz, 3),
                   "frac_of_peak_at_clock": round(tf / (1024 * 32768 / 32 * ghz / 1e3), 4)})
             del stamps, sink
+
+    for valu in (4, 8, 12):
+        blocks = 256  # one 512-thread block per CU: an MFMA and a VALU wavefront per SIMD
+        iters = 60000
+        stamps = torch.zeros(blocks * 8 * 4, dtype=torch.int64, device=dev)
+        sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            ok(lib.gnf4_ceil_mfma_split(iters, blocks, valu, ctypes.c_void_p(stamps.data_ptr()),
+                                        ctypes.c_void_p(sink.data_ptr()), st()), "mfma_split")
+        torch.cuda.synchronize()
+        t = stamps.cpu().numpy().reshape(blocks * 8, 4).astype(np.float64)
+        cyc = t[:, 1] - t[:, 0]
+        is_mfma = (np.arange(blocks * 8) % 8) < 4
+        share = 32.0 * iters * 5 / cyc[is_mfma]
+        emit({"ceiling": "mfma_f16_32x32x16_beside_valu_waves", "waves_per_simd": 2,
+              "valu_per_mfma_slot_in_other_wave": valu, "iters": iters,
+              "mfma_wave_share_median": round(float(np.median(share)), 4),
+              "mfma_wave_share_min": round(float(share.min()), 4),
+              "valu_wave_cycles_over_mfma_wave": round(
+                  float(np.median(cyc[~is_mfma]) / np.median(cyc[is_mfma])), 3)})
+        del stamps, sink
 
     gen = torch.Generator(device=dev).manual_seed(7)
     cases = [("square", 1, 8192, 8192, 8192),

@@ -165,6 +165,66 @@ void launch_mix(int iters, int blocks, uint64_t* stamps, float* sink, void* stre
                      static_cast<hipStream_t>(stream), iters, stamps, sink);
 }
 
+// Two roles in one 512-thread workgroup (two wavefronts per SIMD): waves
+// 0..3 issue only MFMAs (five chains), waves 4..7 only V dependent v_perm_b32
+// per MFMA slot, for the same number of slots.  Each wave stamps its clocks,
+// so the MFMA wavefronts' rate beside VALU-only neighbours can be read.
+constexpr int kSplitThreads = 512;
+
+template <int V>
+__global__ __launch_bounds__(kSplitThreads) void mfma_split_kernel(int iters,
+                                                                   uint64_t* __restrict__ stamps,
+                                                                   float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  half8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (_Float16)(float)((lane + j) & 7) * (_Float16)0.125f;
+    b[j] = (_Float16)(float)((lane * 3 + j) & 7) * (_Float16)0.0625f;
+  }
+  float sum = 0.0f;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  if (wave < 4) {
+    f32x16 acc[kMixChains];
+#pragma unroll
+    for (int c = 0; c < kMixChains; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kMixChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kMixChains; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += acc[c][e];
+  } else {
+    uint32_t r[4] = {(uint32_t)lane, (uint32_t)lane * 7u, (uint32_t)lane * 13u, 5u};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kMixChains; ++c)
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+          r[i & 3] = __builtin_amdgcn_perm(r[(i + 1) & 3], r[i & 3], 0x03020100u + (uint32_t)i);
+    }
+    sum = (float)((r[0] ^ r[1] ^ r[2] ^ r[3]) & 0xffu);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t gt = (uint64_t)blockIdx.x * kSplitThreads + threadIdx.x;
+  if (lane == 0) {
+    uint64_t* s = stamps + 4 * (gt >> 6);
+    s[0] = t0;
+    s[1] = t1;
+    s[2] = r0;
+    s[3] = r1;
+  }
+  sink[gt] = sum;
+}
+
 gnf4_status launched() {
   return hipGetLastError() == hipSuccess ? GNF4_OK : GNF4_ERR_HIP;
 }
@@ -214,5 +274,23 @@ extern "C" gnf4_status gnf4_ceil_mfma_mix(int iters, int blocks, int valu, int l
   GNF4_MIX(8)
   GNF4_MIX(12)
 #undef GNF4_MIX
+  return launched();
+}
+
+extern "C" gnf4_status gnf4_ceil_mfma_split(int iters, int blocks, int valu, uint64_t* stamps,
+                                            float* sink, void* stream) {
+  if (!stamps || !sink || iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > kMaxBlocks ||
+      (valu != 4 && valu != 8 && valu != 12))
+    return GNF4_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (valu == 4)
+    hipLaunchKernelGGL(mfma_split_kernel<4>, dim3(blocks), dim3(kSplitThreads), 0, st, iters,
+                       stamps, sink);
+  else if (valu == 8)
+    hipLaunchKernelGGL(mfma_split_kernel<8>, dim3(blocks), dim3(kSplitThreads), 0, st, iters,
+                       stamps, sink);
+  else
+    hipLaunchKernelGGL(mfma_split_kernel<12>, dim3(blocks), dim3(kSplitThreads), 0, st, iters,
+                       stamps, sink);
   return launched();
 }

@@ -71,6 +71,18 @@ gnf4_status gnf4_ceil_mfma(int iters, int blocks, uint64_t* stamps, float* sink,
 gnf4_status gnf4_ceil_mfma_mix(int iters, int blocks, int valu, int lds_reads, uint64_t* stamps,
                                float* sink, void* stream);
 
+/* Matrix cores beside VALU-only wavefronts: `blocks` blocks of 512 threads
+ * (two waves per SIMD); waves 0..3 of a block issue iters x 5
+ * v_mfma_f32_32x32x16_f16 (five chains), waves 4..7 issue iters x 5 x `valu`
+ * dependent v_perm_b32 (valu 4, 8 or 12) and nothing else.  stamps as
+ * gnf4_ceil_mfma for the blocks * 8 waves (32 * blocks uint64): the MFMA
+ * waves' cycles per MFMA against 32 give their share of the matrix-core
+ * rate with a VALU-only neighbour.  sink: blocks * 512 floats.
+ * GNF4_ERR_INVALID_ARG for other valu values or the limits of
+ * gnf4_ceil_mfma. */
+gnf4_status gnf4_ceil_mfma_split(int iters, int blocks, int valu, uint64_t* stamps, float* sink,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

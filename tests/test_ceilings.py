@@ -25,13 +25,14 @@ def lib():
     h.gnf4_ceil_empty.argtypes = [ci, vp]
     h.gnf4_ceil_mfma.argtypes = [ci, ci, vp, vp, vp]
     h.gnf4_ceil_mfma_mix.argtypes = [ci, ci, ci, ci, vp, vp, vp]
+    h.gnf4_ceil_mfma_split.argtypes = [ci, ci, ci, vp, vp, vp]
     return h
 
 
 def test_every_declared_symbol_is_exported(lib):
     declared = set(re.findall(r"\b(gnf4_ceil_\w+)\s*\(", open(HEADER).read()))
     assert declared == {"gnf4_ceil_read", "gnf4_ceil_empty", "gnf4_ceil_mfma",
-                        "gnf4_ceil_mfma_mix"}
+                        "gnf4_ceil_mfma_mix", "gnf4_ceil_mfma_split"}
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\b(gnf4_ceil_\w+)\b", out))
@@ -54,6 +55,9 @@ def test_bad_arguments_are_refused(lib):
     assert lib.gnf4_ceil_mfma_mix(1, 0, 8, 1, fake, fake, None) == 1
     assert lib.gnf4_ceil_mfma_mix(1, 1, 8, 1, None, fake, None) == 1
     assert lib.gnf4_ceil_mfma_mix(0, 1, 8, 1, fake, fake, None) == 1
+    assert lib.gnf4_ceil_mfma_split(1, 1, 0, fake, fake, None) == 1     # valu not 4/8/12
+    assert lib.gnf4_ceil_mfma_split(1, 1, 8, None, fake, None) == 1
+    assert lib.gnf4_ceil_mfma_split(1, 65537, 8, fake, fake, None) == 1
 
 
 @pytest.mark.gpu
